@@ -11,7 +11,7 @@ def test_hand_worked_golden():
         v = np.array([float(t) for t in rec["v"].split()], dtype=np.float16)
         s16, z16, q = quant.quantize_groups(v[None, :])
         assert int(s16.view(np.uint16)[0]) == int(rec["s"], 16), rec
-        assert float(z16[0]) == float(rec["z"]), rec
+        assert int(z16.view(np.uint16)[0]) == int(np.float16(float(rec["z"])).view(np.uint16)), rec
         assert q[0].tolist() == [int(t) for t in rec["q"].split()], rec
 
 
@@ -38,6 +38,7 @@ def test_half_step_bound_and_ranges():
     s = s16.astype(np.float64)
     z = z16.astype(np.float64)
     assert np.all(s > 0) and np.all((z >= 0) & (z <= 15)) and np.all(z == np.rint(z))
+    assert not np.any(np.signbit(z))                 # zero points are stored as +0, never -0
     assert q.max() <= 15
     wd = quant.dequantize(q, s16, z16)
     unclamped = (q > 0) & (q < 15)
