@@ -1,0 +1,145 @@
+/*
+ * sgemv.h - C ABI of the MI355X (gfx950) SparseGemv library.
+ *
+ * What it computes: y = W' x, where W' is a weight matrix pruned to a
+ * semi-structured N:M pattern along the input dimension (2:4 for important
+ * layers, 1:4 for the others), quantised to INT4 with asymmetric group-wise
+ * scales whose group size is chosen per output channel, and stored in an
+ * index-compressed "2bit-CSR" format; x is FP16 (one vector or a small beam
+ * batch) and accumulation is FP32. Source: the page "Efficient LLM ad
+ * generation via model compression and parallel verification" (Chinese
+ * translation of arXiv 2605.11582), cited as P1 below: §1 ("our core idea"
+ * and the contribution list), §3.2 "Model compression" (adaptive group
+ * quantization, sparsification, eqs. (1)-(3)) and §3.3 "Revised kernel".
+ *
+ * Conventions
+ *  - W is N x K, row-major, row n = output channel, column k = input
+ *    channel; y[b][n] = sum_k W'[n][k] * x[b][k].
+ *  - FP16 values travel as their uint16 bit patterns.
+ *  - Every function returns an int status: SGEMV_OK (0) or a negative error
+ *    code. Nothing aborts, throws or prints. All checks except SGEMV_EHIP
+ *    happen on the host before any HIP call.
+ *  - The library allocates no memory visible to the caller, keeps no global
+ *    state and is re-entrant. Host arrays are owned and sized by the caller;
+ *    device buffers are owned by the caller (e.g. torch tensors).
+ */
+#ifndef SGEMV_H
+#define SGEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SGEMV_OK = 0,
+  SGEMV_EINVAL = -1, /* bad shape, N:M choice, group size, batch, NULL pointer, non-finite weight */
+  SGEMV_ESIZE = -2,  /* inconsistent descriptor, or a size beyond what the kernels support */
+  SGEMV_EALIGN = -3, /* a device pointer is not aligned as required */
+  SGEMV_EHIP = -4    /* the HIP runtime reported an error at launch */
+};
+
+/* Plain-data description of one packed layer. Filled by sgemv_describe and
+ * passed back by pointer; the caller may copy it freely. */
+typedef struct sgemv_desc {
+  int32_t N, K;          /* output rows, input columns (K % 256 == 0)                */
+  int32_t nk;            /* kept elements per group of 4 along K: 2 (2:4) or 1 (1:4) */
+  int32_t rt;            /* kernel layout: rows per tile (one workgroup per tile)    */
+  int32_t tpr;           /* kernel layout: threads per row, power of two in [4, 64]  */
+  int32_t n_tiles;       /* tiles = workgroups launched by sgemv_run                 */
+  int32_t g_min, g_max;  /* smallest and largest group size present                  */
+  int64_t kept;          /* N*K*nk/4 kept elements                                   */
+  int64_t vals_bytes;    /* canonical code array: kept/2 bytes (one nibble each)     */
+  int64_t offs_bytes;    /* canonical offset array: kept/4 bytes (2 bits each)       */
+  int64_t n_groups;      /* sum_n K/g_n: one FP16 scale and one FP16 zero each       */
+  int64_t off_tiles;     /* byte offsets of the blob sections (256-byte aligned)     */
+  int64_t off_perm;
+  int64_t off_vals;
+  int64_t off_offs;
+  int64_t off_sz;
+  int64_t blob_bytes;    /* total size of the kernel-layout blob                     */
+} sgemv_desc;
+
+/* sgemv_describe - validate a layer shape and fill its descriptor.
+ *   N, K         : rows and columns; N >= 1, K >= 256, K % 256 == 0, N*K*nk/4 < 2^31.
+ *   nk           : 2 for 2:4 or 1 for 1:4 (P1 §3.2 "Sparsification").
+ *   group_size   : host int32[N], group size of each row in dense columns; each
+ *                  in {32, 64, 128, 256} and dividing K (P1 §3.2 "Adaptive group
+ *                  quantization": finer groups for sensitive channels).
+ *   rt, tpr      : kernel layout; 0 and 0 pick defaults for this shape. Otherwise
+ *                  tpr in {4,8,16,32,64}, rt*tpr in {64, 128, 256} (workgroup size),
+ *                  at most 16 chunks (32 kept elements each) per thread.
+ *   out          : filled on success.
+ * Errors: EINVAL for bad arguments, ESIZE if the layout constraints cannot be met. */
+int sgemv_describe(int32_t N, int32_t K, int32_t nk, const int32_t* group_size,
+                   int32_t rt, int32_t tpr, sgemv_desc* out);
+
+/* sgemv_select_groups - adaptive group size per output channel (P1 §3.2
+ * "Adaptive group quantization"; sensitivity from the first term of eq. (3)).
+ *   w            : host FP16 bits [N][K], dense weights (pruned inside, as sgemv_pack).
+ *   xcal, T      : host FP16 bits [T][K], calibration activations, T >= 1.
+ *   frac_fine    : fraction of rows given the fine size, in [0, 1], taken to 6
+ *                  decimals; the count is ceil(N * frac_fine).
+ *   g_fine, g_coarse : group sizes (each valid for sgemv_describe).
+ *   group_size_out   : host int32[N].
+ * With c_k = sqrt(sum_t xcal[t][k]^2) and S_n = sum_k |Wp[n][k]| * c_k (FP64,
+ * sequential sums in index order, Wp = W after N:M pruning), the rows with the
+ * largest S_n (ties: lower n) get g_fine and all others g_coarse.
+ * Errors: EINVAL (shape, NULL, non-finite weight or activation, bad sizes). */
+int sgemv_select_groups(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
+                        const uint16_t* xcal, int32_t T, double frac_fine,
+                        int32_t g_fine, int32_t g_coarse, int32_t* group_size_out);
+
+/* sgemv_pack - dense FP16 W -> N:M prune -> asymmetric INT4 group quantisation
+ * -> canonical 2bit-CSR arrays (P1 §1 contributions, first item; §3.2).
+ * Pruning keeps, in every group of 4 consecutive columns of a row, the nk
+ * elements of largest |w| (ties: lower column), offsets ascending. Each
+ * (row, group) is quantised over its kept values: lo = min(0, min v),
+ * hi = max(0, max v); scale = fp16((hi - lo) / 15) (1 if hi == lo, at least
+ * 2^-24); zero = clamp(rint(-lo/scale), 0, 15); code = clamp(rint(v/scale) +
+ * zero, 0, 15); FP64 arithmetic, round half to even.
+ * Output arrays (host, caller-sized from the descriptor):
+ *   vals  [N][K*nk/8]  element j of a row in byte j/2, low nibble when j is even;
+ *   offs  [N][K*nk/16] in-group offset of element j in byte j/4, bits 2(j%4)..+1;
+ *   scale, zero [n_groups] FP16 bits, row-major over (row, group);
+ *   gptr  [N+1] first group of each row; rowptr [N+1] = n*K*nk/4.
+ * Errors: EINVAL (shape, group sizes, NULL, non-finite weight). */
+int sgemv_pack(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
+               const int32_t* group_size, uint8_t* vals, uint8_t* offs,
+               uint16_t* scale, uint16_t* zero, int32_t* gptr, int32_t* rowptr);
+
+/* sgemv_layout - canonical arrays -> kernel-layout blob (host). The blob holds
+ * the same bits reordered for coalesced 16/8/4-byte loads: tile table, row
+ * permutation (rows sorted by group size), codes, offsets and packed
+ * scale|zero<<16 words; the exact rules are written out with the oracle's
+ * layout module and in the design notes. Group sizes are taken from gptr.
+ *   d        : descriptor from sgemv_describe for the same group sizes.
+ *   blob     : host buffer of d->blob_bytes bytes, fully written.
+ * Errors: EINVAL (NULL, gptr inconsistent with d), ESIZE. */
+int sgemv_layout(const sgemv_desc* d, const uint8_t* vals, const uint8_t* offs,
+                 const uint16_t* scale, const uint16_t* zero, const int32_t* gptr,
+                 void* blob);
+
+/* sgemv_run - y = W' x on the GPU (P1 §3.3 "Revised kernel": INT4 weight-only
+ * GEMV with mixed N:M sparsity).
+ *   d        : descriptor of the packed layer.
+ *   blob_dev : device copy of the blob, 256-byte aligned, d->blob_bytes bytes.
+ *   x_dev    : device FP16 [B][K] row-major, 16-byte aligned.
+ *   y_dev    : device FP16 [B][N] row-major, 2-byte aligned; fully overwritten.
+ *   B        : batch (beam width), 1..16.
+ *   hip_stream : hipStream_t to enqueue on (NULL = default stream).
+ * Enqueues one kernel and returns without synchronising. x and y must not
+ * overlap the blob or each other. Deterministic: the same inputs give the
+ * same bits on every call. Errors: EINVAL, ESIZE, EALIGN (host checks), EHIP. */
+int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* x_dev,
+              void* y_dev, int32_t B, void* hip_stream);
+
+/* sgemv_strerror - static description of a status code (never NULL). */
+const char* sgemv_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMV_H */

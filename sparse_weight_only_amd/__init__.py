@@ -1,0 +1,11 @@
+"""MI355X-native SparseGemv: N:M-sparse INT4 weight-only GEMV in 2bit-CSR form.
+
+The package is a thin ctypes binding over the in-tree C-ABI library
+``_lib/libsgemv.so`` (host packer + gfx950 HIP kernels). Every step of the
+computation runs in that library; Python only marshals arguments, and
+PyTorch only supplies device memory and streams.
+"""
+from .sgemv import (  # noqa: F401
+    SgemvError, Desc, lib, lib_path, describe, select_groups, pack, layout, run, strerror,
+    SparseGemvLayer, algorithmic_bytes,
+)

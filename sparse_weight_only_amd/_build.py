@@ -1,0 +1,63 @@
+"""Build the in-tree C-ABI library ``_lib/libsgemv.so`` for gfx950.
+
+Host sources (packer, layout) are compiled by g++ with -ffp-contract=off so
+every FP64 operation of the packer is rounded on its own; the HIP source is
+compiled by hipcc for gfx950 with packed-FP32 instructions disabled; hipcc
+links the shared library against the HIP runtime.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+OUT_DIR = os.path.join(HERE, "_lib")
+LIB = os.path.join(OUT_DIR, "libsgemv.so")
+HOST_SRCS = ["host_pack.cpp", "host_layout.cpp"]
+HIP_SRCS = ["sgemv_kernels.hip"]
+
+
+def _hipcc() -> str:
+    for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found: the SparseGemv library needs ROCm's hipcc")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("build failed:\n" + " ".join(cmd) + "\n" + out)
+    if verbose and out.strip():
+        print(out, flush=True)
+
+
+def build(verbose: bool = False, arch: str = "gfx950") -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    bdir = os.path.join(OUT_DIR, "obj")
+    os.makedirs(bdir, exist_ok=True)
+    objs = []
+    for s in HOST_SRCS:
+        o = os.path.join(bdir, s + ".o")
+        _run(["g++", "-std=c++17", "-O2", "-fPIC", "-ffp-contract=off", "-fno-fast-math",
+              "-Wall", "-Wextra", "-c", os.path.join(CSRC, s), "-o", o], verbose)
+        objs.append(o)
+    hipcc = _hipcc()
+    for s in HIP_SRCS:
+        o = os.path.join(bdir, s + ".o")
+        _run([hipcc, f"--offload-arch={arch}", "-std=c++17", "-O3", "-fPIC", "-ffp-contract=off",
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              "-Wall", "-c", os.path.join(CSRC, s), "-o", o], verbose)
+        objs.append(o)
+    tmp = LIB + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,198 @@
+"""ctypes binding of the SparseGemv C ABI (``include/sgemv.h``).
+
+Functions keep the C names without the ``sgemv_`` prefix and only marshal
+arguments: NumPy arrays for host buffers, raw device pointers (ints) for
+device buffers, a raw ``hipStream_t`` (int) for the stream. Errors raise
+``SgemvError``. ``SparseGemvLayer`` bundles describe -> pack -> layout ->
+upload with torch-owned device memory.
+
+The library must have been built (``__graft_entry__.build()`` or
+``python sparse_weight_only_amd/_build.py``); nothing here falls back to
+another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "_lib", "libsgemv.so")
+_lib = None
+
+SGEMV_OK, SGEMV_EINVAL, SGEMV_ESIZE, SGEMV_EALIGN, SGEMV_EHIP = 0, -1, -2, -3, -4
+
+
+class SgemvError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (status {code})")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("nk", ctypes.c_int32),
+        ("rt", ctypes.c_int32), ("tpr", ctypes.c_int32), ("n_tiles", ctypes.c_int32),
+        ("g_min", ctypes.c_int32), ("g_max", ctypes.c_int32),
+        ("kept", ctypes.c_int64), ("vals_bytes", ctypes.c_int64), ("offs_bytes", ctypes.c_int64),
+        ("n_groups", ctypes.c_int64), ("off_tiles", ctypes.c_int64), ("off_perm", ctypes.c_int64),
+        ("off_vals", ctypes.c_int64), ("off_offs", ctypes.c_int64), ("off_sz", ctypes.c_int64),
+        ("blob_bytes", ctypes.c_int64),
+    ]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load the C-ABI library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"SparseGemv library not built: {_LIB_PATH} is missing "
+                               "(run __graft_entry__.build())")
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.sgemv_describe.argtypes = [i32, i32, i32, P, i32, i32, ctypes.POINTER(Desc)]
+        L.sgemv_select_groups.argtypes = [P, i32, i32, i32, P, i32, f64, i32, i32, P]
+        L.sgemv_pack.argtypes = [P, i32, i32, i32, P, P, P, P, P, P, P]
+        L.sgemv_layout.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P, P]
+        L.sgemv_run.argtypes = [ctypes.POINTER(Desc), P, P, P, i32, P]
+        L.sgemv_strerror.argtypes = [ctypes.c_int]
+        L.sgemv_strerror.restype = ctypes.c_char_p
+        for f in ("sgemv_describe", "sgemv_select_groups", "sgemv_pack", "sgemv_layout", "sgemv_run"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().sgemv_strerror(int(code)).decode()
+
+
+def _check(code: int, where: str):
+    if code != SGEMV_OK:
+        raise SgemvError(code, where)
+
+
+def _host(a: np.ndarray, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def describe(N: int, K: int, nk: int, group_size, rt: int = 0, tpr: int = 0) -> Desc:
+    gs = _host(np.asarray(group_size, dtype=np.int32), np.int32)
+    d = Desc()
+    _check(lib().sgemv_describe(N, K, nk, _ptr(gs), rt, tpr, ctypes.byref(d)), "sgemv_describe")
+    return d
+
+
+def select_groups(w16: np.ndarray, nk: int, xcal16: np.ndarray, frac_fine: float = 0.10,
+                  g_fine: int = 32, g_coarse: int = 128) -> np.ndarray:
+    w = _host(np.asarray(w16).view(np.uint16), np.uint16)
+    xc = _host(np.asarray(xcal16).view(np.uint16), np.uint16)
+    N, K = w.shape
+    out = np.empty(N, dtype=np.int32)
+    _check(lib().sgemv_select_groups(_ptr(w), N, K, nk, _ptr(xc), xc.shape[0], float(frac_fine),
+                                     g_fine, g_coarse, _ptr(out)), "sgemv_select_groups")
+    return out
+
+
+def pack(w16: np.ndarray, nk: int, group_size) -> dict:
+    """Dense FP16 [N, K] -> canonical 2bit-CSR arrays (dict of NumPy arrays)."""
+    w = _host(np.asarray(w16).view(np.uint16), np.uint16)
+    N, K = w.shape
+    gs = _host(np.asarray(group_size, dtype=np.int32), np.int32)
+    if gs.shape != (N,):
+        raise ValueError("group_size must have one entry per row")
+    if K % 256 or nk not in (1, 2):
+        _check(SGEMV_EINVAL, "sgemv_pack")
+    kpr = K * nk // 4
+    ng = int(np.sum(K // np.maximum(gs.astype(np.int64), 1)))
+    vals = np.empty((N, kpr // 2), dtype=np.uint8)
+    offs = np.empty((N, kpr // 4), dtype=np.uint8)
+    scale = np.empty(max(ng, 1), dtype=np.uint16)
+    zero = np.empty(max(ng, 1), dtype=np.uint16)
+    gptr = np.empty(N + 1, dtype=np.int32)
+    rowptr = np.empty(N + 1, dtype=np.int32)
+    _check(lib().sgemv_pack(_ptr(w), N, K, nk, _ptr(gs), _ptr(vals), _ptr(offs), _ptr(scale),
+                            _ptr(zero), _ptr(gptr), _ptr(rowptr)), "sgemv_pack")
+    return {"N": N, "K": K, "nk": nk, "group_size": gs, "vals": vals, "offs": offs,
+            "scale": scale[:ng], "zero": zero[:ng], "gptr": gptr, "rowptr": rowptr}
+
+
+def layout(desc: Desc, canon: dict) -> np.ndarray:
+    """Canonical arrays -> kernel-layout blob (host uint8 array of desc.blob_bytes)."""
+    blob = np.empty(desc.blob_bytes, dtype=np.uint8)
+    arrs = [_host(canon["vals"], np.uint8), _host(canon["offs"], np.uint8),
+            _host(canon["scale"], np.uint16), _host(canon["zero"], np.uint16),
+            _host(canon["gptr"], np.int32)]
+    _check(lib().sgemv_layout(ctypes.byref(desc), *[_ptr(a) for a in arrs], _ptr(blob)), "sgemv_layout")
+    return blob
+
+
+def run(desc: Desc, blob_dev: int, x_dev: int, y_dev: int, B: int, stream: int = 0) -> None:
+    """Enqueue y = W' x on ``stream`` (raw device pointers as ints)."""
+    _check(lib().sgemv_run(ctypes.byref(desc), ctypes.c_void_p(blob_dev), ctypes.c_void_p(x_dev),
+                           ctypes.c_void_p(y_dev), B, ctypes.c_void_p(stream)), "sgemv_run")
+
+
+def algorithmic_bytes(desc: Desc, B: int) -> int:
+    """Bytes the method must move per call: codes + offsets + FP16 scale/zero + x + y."""
+    return int(desc.vals_bytes + desc.offs_bytes + 4 * desc.n_groups + 2 * B * desc.K + 2 * B * desc.N)
+
+
+class SparseGemvLayer:
+    """One packed layer resident on the GPU (torch-owned device blob)."""
+
+    def __init__(self, desc: Desc, canon: dict, blob_host: np.ndarray, device="cuda"):
+        import torch
+        self.desc = desc
+        self.canon = canon
+        self.blob_host = blob_host
+        self.blob = torch.from_numpy(blob_host).to(device)
+        if self.blob.data_ptr() % 256:
+            raise RuntimeError("device blob is not 256-byte aligned")
+
+    @classmethod
+    def from_dense(cls, w16: np.ndarray, nk: int, group_size=None, xcal16: Optional[np.ndarray] = None,
+                   frac_fine: float = 0.10, g_fine: int = 32, g_coarse: int = 128,
+                   rt: int = 0, tpr: int = 0, device="cuda") -> "SparseGemvLayer":
+        w16 = np.asarray(w16, dtype=np.float16)
+        N, K = w16.shape
+        if group_size is None:
+            group_size = np.full(N, g_coarse, dtype=np.int32)
+        elif isinstance(group_size, str) and group_size == "adaptive":
+            if xcal16 is None:
+                raise ValueError("adaptive groups need a calibration batch")
+            group_size = select_groups(w16, nk, xcal16, frac_fine, g_fine, g_coarse)
+        canon = pack(w16, nk, group_size)
+        desc = describe(N, K, nk, group_size, rt, tpr)
+        return cls(desc, canon, layout(desc, canon), device)
+
+    def run(self, x, y=None, stream=None):
+        """y = W' x for a torch FP16 tensor x of shape [K] or [B, K] on the device."""
+        import torch
+        squeeze = x.dim() == 1
+        x2 = x.reshape(1, -1) if squeeze else x
+        if x2.dtype != torch.float16 or not x2.is_contiguous() or x2.shape[1] != self.desc.K:
+            raise ValueError("x must be a contiguous FP16 tensor with K columns")
+        B = x2.shape[0]
+        if y is None:
+            y = torch.empty((B, self.desc.N), dtype=torch.float16, device=x.device)
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        run(self.desc, self.blob.data_ptr(), x2.data_ptr(), y.data_ptr(), B, s.cuda_stream)
+        return y.reshape(-1) if squeeze else y

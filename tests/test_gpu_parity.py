@@ -1,0 +1,163 @@
+"""GPU parity: the HIP SparseGemv kernels through the C ABI against the FP64 oracle.
+
+Bars: bit-exact where the arithmetic is exact (grid weights with x in
+{-1,0,1}; one-hot x), normalised error <= 2e-3 elsewhere, guard bands intact,
+identical bits on repeated runs.
+"""
+import numpy as np
+import pytest
+
+import synth
+import sparse_weight_only_amd as sg
+from oracle import gemv as ogemv
+from gpu_util import TOL, say, group_sizes, make_layer, run_checked, oracle_y, check_pack_matches_oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sg.lib()
+
+
+def grid_weights(N, K, nk, g, rng, s=2.0 ** -6):
+    """Values k*s, k in [-8, 7], with every quantisation group keeping -8s and 7s."""
+    W = rng.integers(-8, 8, (N, K)).astype(np.float64)
+    for c0 in range(0, K, g):
+        W[:, c0: c0 + 4] = [-8, 7, 0, 0] if nk == 2 else [-8, 0, 0, 0]
+        if nk == 1:
+            W[:, c0 + 4: c0 + 8] = [7, 0, 0, 0]
+    return (W * s).astype(np.float16)
+
+
+@pytest.mark.parametrize("nk", [2, 1])
+@pytest.mark.parametrize("N,K,gs_kind,rt,tpr", [
+    (1024, 1024, "u128", 0, 0), (300, 4096, "mixed", 0, 0), (77, 11008, "mixed", 0, 0),
+    (513, 2048, "all", 16, 16), (40, 768, "mixed", 2, 32), (1, 256, "u128", 0, 0),
+    (130, 1280, "all", 1, 64), (96, 512, "u32", 64, 4),
+])
+def test_exact_arithmetic_bit_exact(nk, N, K, gs_kind, rt, tpr):
+    rng = np.random.default_rng(N + K + nk)
+    gchoices = {"u128": [128], "u32": [32], "mixed": [32, 128], "all": [32, 64, 128, 256]}[gs_kind]
+    gchoices = [g for g in gchoices if K % g == 0]
+    gs = rng.choice(gchoices, N).astype(np.int32)
+    if tpr and max(gs) > 128 // nk and (tpr % (max(gs) // (128 // nk))):
+        gs = np.minimum(gs, 128)
+    W = np.zeros((N, K), np.float16)
+    for g in np.unique(gs):
+        rows = gs == g
+        W[rows] = grid_weights(int(rows.sum()), K, nk, int(g), rng)
+    say(f"case exact nk={nk} N={N} K={K} groups={gs_kind} rt={rt} tpr={tpr}")
+    layer = make_layer(W, nk, gs, rt, tpr)
+    co = check_pack_matches_oracle(W, nk, gs, layer.canon)
+    assert np.all(np.abs(co["scale"].view(np.float16).astype(np.float64) - 2.0 ** -6) == 0)
+    for B in (1, 3):
+        X = np.zeros((B, K), np.float16)
+        for b in range(B):
+            idx = rng.choice(K, size=min(64, K), replace=False)
+            X[b, idx] = rng.choice([-1.0, 1.0], len(idx))
+        y = run_checked(layer, X)
+        y_ref, D, _ = oracle_y(layer.canon, X)
+        want = y_ref.astype(np.float16)
+        assert np.array_equal(want.astype(np.float64), y_ref), "reference not exact"
+        assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), f"B={B}"
+
+
+@pytest.mark.parametrize("L", synth.cfg1() + synth.cfg2() + synth.cfg3(), ids=lambda L: L.name)
+def test_one_hot_columns_bit_exact(L):
+    W = L.W()
+    gs = group_sizes(L, W)
+    say(f"case one-hot {L.name}")
+    layer = make_layer(W, L.nk, gs)
+    Wd = ogemv.dequant_dense(layer.canon)
+    rng = np.random.default_rng(5)
+    cols = np.concatenate([[0, L.K - 1], rng.choice(L.K, 14, replace=False)])
+    X = np.zeros((16, L.K), np.float16)
+    X[np.arange(16), cols] = 1.0
+    y = run_checked(layer, X)
+    want = Wd[:, cols].T.astype(np.float16)
+    assert np.array_equal(y.view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("L", synth.cfg1() + synth.cfg2() + synth.cfg3(), ids=lambda L: L.name)
+def test_configs_within_tolerance(L):
+    W = L.W()
+    gs = group_sizes(L, W)
+    say(f"case config {L.name}")
+    layer = make_layer(W, L.nk, gs)
+    check_pack_matches_oracle(W, L.nk, gs, layer.canon)
+    X = L.X(1)
+    y = run_checked(layer, X)
+    y_ref, D, _ = oracle_y(layer.canon, X)
+    err = ogemv.normalized_error(y, y_ref, D)
+    say(f"  {L.name}: normalised error {err:.3e}")
+    assert err <= TOL
+    y2 = run_checked(layer, X)
+    assert np.array_equal(y.view(np.uint16), y2.view(np.uint16)), "not deterministic"
+
+
+@pytest.mark.parametrize("L", synth.cfg5(), ids=lambda L: L.name)
+def test_beam_batches_within_tolerance(L):
+    W = L.W()
+    gs = group_sizes(L, W)
+    say(f"case beam {L.name}")
+    layer = make_layer(W, L.nk, gs)
+    for B in synth.CFG5_BATCHES:
+        X = L.X(B)
+        y = run_checked(layer, X)
+        y_ref, D, _ = oracle_y(layer.canon, X)
+        err = ogemv.normalized_error(y, y_ref, D)
+        say(f"  B={B}: normalised error {err:.3e}")
+        assert err <= TOL
+        # each batch row equals the batch-1 result of that row (same kernel arithmetic per row)
+        y1 = run_checked(layer, X[B - 1: B])
+        assert ogemv.normalized_error(y1, y_ref[B - 1: B], D[B - 1: B]) <= TOL
+
+
+def test_decoder_set_sampled_layers_back_to_back():
+    """Layers 0 (2:4), 4 (1:4) and 31 (2:4) of the 32-layer set, all 7 projections, on one stream."""
+    Ls = [L for L in synth.cfg4() if L.layer in (0, 4, 31)]
+    import torch
+    layers, xs, ys = [], [], []
+    for L in Ls:
+        W = L.W()
+        layers.append((L, make_layer(W, L.nk, group_sizes(L, W))))
+    say(f"case decoder set, {len(layers)} GEMVs back to back")
+    for L, layer in layers:
+        x = torch.from_numpy(L.X(1)).cuda()
+        y = torch.empty((1, L.N), dtype=torch.float16, device="cuda")
+        sg.run(layer.desc, layer.blob.data_ptr(), x.data_ptr(), y.data_ptr(), 1,
+               torch.cuda.current_stream().cuda_stream)
+        xs.append(x)
+        ys.append(y)
+    torch.cuda.synchronize()
+    for (L, layer), y in zip(layers, ys):
+        y_ref, D, _ = oracle_y(layer.canon, L.X(1))
+        err = ogemv.normalized_error(y.cpu().numpy(), y_ref, D)
+        assert err <= TOL, (L.name, err)
+
+
+@pytest.mark.parametrize("B", [1, 2, 5, 16])
+def test_odd_shapes_and_batches(B):
+    rng = np.random.default_rng(B)
+    for (N, K, nk) in [(1, 256, 2), (3, 256, 1), (257, 1536, 2), (129, 2816, 1)]:
+        W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+        gs = rng.choice([32, 64, 128], N).astype(np.int32)
+        say(f"case odd N={N} K={K} nk={nk} B={B}")
+        layer = make_layer(W, nk, gs)
+        X = rng.standard_normal((B, K)).astype(np.float16)
+        X[:, :8] = 0
+        y = run_checked(layer, X)
+        y_ref, D, _ = oracle_y(layer.canon, X)
+        assert ogemv.normalized_error(y, y_ref, D) <= TOL
+
+
+def test_zero_input_gives_zero_output():
+    rng = np.random.default_rng(9)
+    W = (rng.standard_normal((64, 512)) * 0.02).astype(np.float16)
+    layer = make_layer(W, 2, np.full(64, 128, np.int32))
+    y = run_checked(layer, np.zeros((2, 512), np.float16))
+    assert np.all(y.view(np.uint16) == 0)
