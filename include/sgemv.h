@@ -49,6 +49,8 @@ typedef struct sgemv_desc {
   int32_t tpr;           /* kernel layout: threads per row, power of two in [4, 64]  */
   int32_t n_tiles;       /* tiles = workgroups launched by sgemv_run                 */
   int32_t g_min, g_max;  /* smallest and largest group size present                  */
+  int32_t class_rows[4]; /* rows with group size 32, 64, 128, 256 (sorted in that order) */
+  int32_t reserved;      /* zero                                                     */
   int64_t kept;          /* N*K*nk/4 kept elements                                   */
   int64_t vals_bytes;    /* canonical code array: kept/2 bytes (one nibble each)     */
   int64_t offs_bytes;    /* canonical offset array: kept/4 bytes (2 bits each)       */

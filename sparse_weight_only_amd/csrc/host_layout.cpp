@@ -46,18 +46,6 @@ void order_and_tiles(const int32_t* gs, int32_t N, int32_t rt, std::vector<int32
   }
 }
 
-bool layout_ok(int32_t C, int cpc, int32_t tpr, int32_t rt, int g_max) {
-  if (tpr < 4 || tpr > 64 || (tpr & (tpr - 1))) return false;
-  int32_t wg = rt * tpr;
-  if (rt < 1 || (wg != 64 && wg != 128 && wg != 256)) return false;
-  if ((C + tpr - 1) / tpr > kMaxChunksPerThread) return false;
-  if (g_max > cpc) {
-    int share = g_max / cpc;                 // chunks sharing one scale/zero word
-    if (tpr % share || C % share) return false;
-  }
-  return true;
-}
-
 }  // namespace
 
 extern "C" int sgemv_describe(int32_t N, int32_t K, int32_t nk, const int32_t* group_size,
@@ -77,13 +65,15 @@ extern "C" int sgemv_describe(int32_t N, int32_t K, int32_t nk, const int32_t* g
   const int cpc = cols_per_chunk(nk);
   const int32_t C = K * nk / 128;
   if (rt == 0 && tpr == 0) {
-    // default: 256-thread workgroups, the fewest k-lanes giving <= 6 chunks per thread
-    for (tpr = 4; tpr <= 64; tpr *= 2)
-      if ((C + tpr - 1) / tpr <= 6 && layout_ok(C, cpc, tpr, 256 / tpr, g_max)) break;
-    if (tpr > 64) tpr = 64;
-    rt = 256 / tpr;
+    // default: one row per wave (or as many lanes as the row has chunks, at
+    // least 4) and 512-thread workgroups, fewer if the register budget asks
+    tpr = 4;
+    while (tpr < 64 && tpr < C) tpr *= 2;
+    const int32_t ch = (C + tpr - 1) / tpr;
+    const int wg = std::min(512, wg_limit(ch));
+    rt = std::max(1, wg / tpr);
   }
-  if (!layout_ok(C, cpc, tpr, rt, g_max)) return SGEMV_ESIZE;
+  if (!layout_params_ok(K, C, cpc, tpr, rt, g_max)) return SGEMV_ESIZE;
   std::vector<int32_t> perm;
   std::vector<Tile> tiles;
   order_and_tiles(group_size, N, rt, perm, tiles);
@@ -92,6 +82,7 @@ extern "C" int sgemv_describe(int32_t N, int32_t K, int32_t nk, const int32_t* g
   d.N = N; d.K = K; d.nk = nk; d.rt = rt; d.tpr = tpr;
   d.n_tiles = (int32_t)tiles.size();
   d.g_min = g_min; d.g_max = g_max;
+  for (int32_t n = 0; n < N; ++n) d.class_rows[ilog2(group_size[n] / 32)] += 1;
   d.kept = (int64_t)N * K * nk / 4;
   d.vals_bytes = d.kept / 2;
   d.offs_bytes = d.kept / 4;

@@ -9,7 +9,7 @@
 namespace sgemv {
 
 constexpr int kChunkElems = 32;            // kept elements per chunk (16 B codes, 8 B offsets)
-constexpr int kMaxChunksPerThread = 16;    // register budget of the kernels
+constexpr int kMaxChunksPerThread = 8;     // register budget of the kernels
 constexpr int64_t kAlign = 256;            // blob section alignment
 
 inline int cols_per_chunk(int nk) { return 128 / nk; }          // 64 at 2:4, 128 at 1:4
@@ -58,5 +58,28 @@ inline double f16_to_f64(uint16_t h) {
 }
 
 inline bool f16_finite(uint16_t h) { return ((h >> 10) & 31) != 31; }
+
+// Workgroup limit of the batch-1 kernel for a lane owning ch chunks (its
+// register budget): 1024 threads up to 2 chunks, 512 up to 4, 256 up to 8.
+inline int wg_limit(int ch) { return ch <= 2 ? 1024 : ch <= 4 ? 512 : 256; }
+
+// Layout parameters the kernels accept: tpr lanes per row (a power of two in
+// [4, 64], so a row's lanes sit in one wave), rt*tpr threads per workgroup (a
+// power of two in [64, 1024] within the register budget), at most 8 chunks
+// per lane, at most 8 x blocks of 8 columns staged per lane, and chunks that
+// share a scale word owned by the same iteration.
+inline bool layout_params_ok(int32_t K, int32_t C, int cpc, int32_t tpr, int32_t rt, int g_max) {
+  if (tpr < 4 || tpr > 64 || (tpr & (tpr - 1))) return false;
+  const int32_t ch = (C + tpr - 1) / tpr;
+  if (ch > kMaxChunksPerThread) return false;
+  const int32_t wg = rt * tpr;
+  if (rt < 1 || wg < 64 || wg > wg_limit(ch) || (wg & (wg - 1))) return false;
+  if ((K / 8 + wg - 1) / wg > 8) return false;      // x blocks staged per lane
+  if (g_max > cpc) {
+    const int share = g_max / cpc;   // chunks sharing one scale/zero word
+    if (tpr % share || C % share) return false;
+  }
+  return true;
+}
 
 }  // namespace sgemv

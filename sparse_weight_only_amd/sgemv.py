@@ -36,6 +36,7 @@ class Desc(ctypes.Structure):
         ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("nk", ctypes.c_int32),
         ("rt", ctypes.c_int32), ("tpr", ctypes.c_int32), ("n_tiles", ctypes.c_int32),
         ("g_min", ctypes.c_int32), ("g_max", ctypes.c_int32),
+        ("class_rows", ctypes.c_int32 * 4), ("reserved", ctypes.c_int32),
         ("kept", ctypes.c_int64), ("vals_bytes", ctypes.c_int64), ("offs_bytes", ctypes.c_int64),
         ("n_groups", ctypes.c_int64), ("off_tiles", ctypes.c_int64), ("off_perm", ctypes.c_int64),
         ("off_vals", ctypes.c_int64), ("off_offs", ctypes.c_int64), ("off_sz", ctypes.c_int64),
@@ -43,7 +44,7 @@ class Desc(ctypes.Structure):
     ]
 
     def as_dict(self) -> dict:
-        return {f: getattr(self, f) for f, _ in self._fields_}
+        return {f: (list(getattr(self, f)) if f == "class_rows" else getattr(self, f)) for f, _ in self._fields_}
 
 
 def lib_path() -> str:
