@@ -123,6 +123,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    # reference copy of known size (64 MiB read + 64 MiB written): the scale for
+    # HBM byte counters collected over this same command
+    ref_a = torch.empty(64 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    ref_b = torch.empty_like(ref_a)
+    ref_b.copy_(ref_a)
+    torch.cuda.synchronize()
+    del ref_a, ref_b
 
     layers = synth.cfg3()
     t_pack = time.perf_counter()

@@ -70,8 +70,10 @@ typedef struct sgemv_desc {
  *                  in {32, 64, 128, 256} and dividing K (P1 §3.2 "Adaptive group
  *                  quantization": finer groups for sensitive channels).
  *   rt, tpr      : kernel layout; 0 and 0 pick defaults for this shape. Otherwise
- *                  tpr in {4,8,16,32,64}, rt*tpr in {64, 128, 256} (workgroup size),
- *                  at most 16 chunks (32 kept elements each) per thread.
+ *                  tpr in {4,8,16,32,64}; rt*tpr a power of two in [64, 1024], run
+ *                  by workgroups of min(256, rt*tpr) lanes owning rt*tpr/256 rows
+ *                  each; at most 8 chunks (32 kept elements each) of a row per
+ *                  lane and 8 per lane in all; at most 8 16-byte x blocks per lane.
  *   out          : filled on success.
  * Errors: EINVAL for bad arguments, ESIZE if the layout constraints cannot be met. */
 int sgemv_describe(int32_t N, int32_t K, int32_t nk, const int32_t* group_size,
@@ -136,6 +138,23 @@ int sgemv_layout(const sgemv_desc* d, const uint8_t* vals, const uint8_t* offs,
  * same bits on every call. Errors: EINVAL, ESIZE, EALIGN (host checks), EHIP. */
 int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* x_dev,
               void* y_dev, int32_t B, void* hip_stream);
+
+/* What sgemv_run enqueues for a layer and a batch (filled by sgemv_plan). */
+typedef struct sgemv_plan_t {
+  int64_t grid;                /* workgroups launched                                  */
+  int64_t lds_bytes;           /* dynamic LDS per workgroup (staged x planes)          */
+  int32_t block;               /* lanes per workgroup                                  */
+  int32_t pass_log2;           /* log2 of workgroups per tile (beam-batch kernel)      */
+  int32_t rows_per_lane;       /* rows each lane accumulates (batch-1 kernel)          */
+  int32_t chunks_per_row_lane; /* 32-element chunks of one row per lane                */
+  int32_t phase_iters;         /* chunk iterations whose x is staged at once           */
+  int32_t batched;             /* 1 if the beam-batch kernel runs, else 0              */
+} sgemv_plan_t;
+
+/* sgemv_plan - describe the launch sgemv_run would make for (d, B) without
+ * making any HIP call (for occupancy planning and host-side checks).
+ * Errors: EINVAL (NULL, B outside 1..16), ESIZE (inconsistent descriptor). */
+int sgemv_plan(const sgemv_desc* d, int32_t B, sgemv_plan_t* out);
 
 /* sgemv_strerror - static description of a status code (never NULL). */
 const char* sgemv_strerror(int code);

@@ -65,13 +65,11 @@ extern "C" int sgemv_describe(int32_t N, int32_t K, int32_t nk, const int32_t* g
   const int cpc = cols_per_chunk(nk);
   const int32_t C = K * nk / 128;
   if (rt == 0 && tpr == 0) {
-    // default: one row per wave (or as many lanes as the row has chunks, at
-    // least 4) and 512-thread workgroups, fewer if the register budget asks
-    tpr = 4;
-    while (tpr < 64 && tpr < C) tpr *= 2;
-    const int32_t ch = (C + tpr - 1) / tpr;
-    const int wg = std::min(512, wg_limit(ch));
-    rt = std::max(1, wg / tpr);
+    // default: 256-lane workgroups, 32 lanes per row (two rows per wave), or
+    // 64 when a row has more than 128 chunks (at most 4 chunks per lane)
+    tpr = C > 128 ? 64 : 32;
+    while (tpr > 4 && tpr / 2 >= C) tpr /= 2;
+    rt = 256 / tpr;
   }
   if (!layout_params_ok(K, C, cpc, tpr, rt, g_max)) return SGEMV_ESIZE;
   std::vector<int32_t> perm;

@@ -59,22 +59,33 @@ inline double f16_to_f64(uint16_t h) {
 
 inline bool f16_finite(uint16_t h) { return ((h >> 10) & 31) != 31; }
 
-// Workgroup limit of the batch-1 kernel for a lane owning ch chunks (its
-// register budget): 1024 threads up to 2 chunks, 512 up to 4, 256 up to 8.
-inline int wg_limit(int ch) { return ch <= 2 ? 1024 : ch <= 4 ? 512 : 256; }
+// Kernel geometry of a layout: a tile of rt rows with tpr lanes per row is
+// one workgroup of min(256, rt*tpr) lanes, each lane owning rpl rows.
+struct Geometry { int wg, rpl, iters, imax, xmax; };
+inline int bucket(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
+inline Geometry geometry(int32_t K, int32_t C, int32_t tpr, int32_t rt) {
+  Geometry g;
+  const int32_t slots = rt * tpr;
+  g.wg = slots < 256 ? slots : 256;
+  g.rpl = slots / g.wg;
+  g.iters = (C + tpr - 1) / tpr;
+  g.imax = bucket(g.iters);
+  g.xmax = ((K / 8 + g.wg - 1) / g.wg) <= 2 ? 2 : 8;
+  return g;
+}
 
 // Layout parameters the kernels accept: tpr lanes per row (a power of two in
-// [4, 64], so a row's lanes sit in one wave), rt*tpr threads per workgroup (a
-// power of two in [64, 1024] within the register budget), at most 8 chunks
-// per lane, at most 8 x blocks of 8 columns staged per lane, and chunks that
-// share a scale word owned by the same iteration.
+// [4, 64], so a row's lanes sit in one wave); rt*tpr a power of two in
+// [64, 1024] giving 1, 2 or 4 rows per lane; at most 8 chunks per row-lane and
+// 8 chunks per lane in all; at most 8 x blocks of 8 columns staged per lane;
+// chunks that share a scale word owned by the same iteration.
 inline bool layout_params_ok(int32_t K, int32_t C, int cpc, int32_t tpr, int32_t rt, int g_max) {
   if (tpr < 4 || tpr > 64 || (tpr & (tpr - 1))) return false;
-  const int32_t ch = (C + tpr - 1) / tpr;
-  if (ch > kMaxChunksPerThread) return false;
-  const int32_t wg = rt * tpr;
-  if (rt < 1 || wg < 64 || wg > wg_limit(ch) || (wg & (wg - 1))) return false;
-  if ((K / 8 + wg - 1) / wg > 8) return false;      // x blocks staged per lane
+  const int32_t slots = rt * tpr;
+  if (rt < 1 || slots < 64 || slots > 1024 || (slots & (slots - 1))) return false;
+  const Geometry g = geometry(K, C, tpr, rt);
+  if (g.iters > kMaxChunksPerThread || g.rpl * g.imax > kMaxChunksPerThread) return false;
+  if ((K / 8 + g.wg - 1) / g.wg > 8) return false;
   if (g_max > cpc) {
     const int share = g_max / cpc;   // chunks sharing one scale/zero word
     if (tpr % share || C % share) return false;

@@ -328,83 +328,141 @@ __device__ __forceinline__ void tile_body(const KParams& p, u32x4* xs, int row0,
   }
 }
 
-// Batch-1 tile: x is staged once for the whole row, and its loads are issued
-// before the weight loads so that the LDS staging and the barrier do not wait
-// for the weights (vector loads complete in issue order). Every load is
-// unconditional (lanes without work load a valid neighbouring address and
-// drop the data), so the number of loads in flight is known statically.
-template <int NK, int G, int MAXCH, int XMAX>
+// Raw buffer loads: 32-bit lane offsets from a per-workgroup base held in
+// SGPRs; offsets at or beyond the range return zeros without touching memory.
+constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit buffer, gfx9-family layout
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+// CPOL: 0 = default caching, 2 = non-temporal (the weights are read once).
+constexpr int kCached = 0, kStream = 2;
+template <int CPOL = kCached>
+__device__ __forceinline__ u32x4 bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL));
+}
+template <int CPOL = kCached>
+__device__ __forceinline__ u32x2 bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CPOL));
+}
+template <int CPOL = kCached>
+__device__ __forceinline__ uint32_t bload1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CPOL);
+}
+
+// Batch-1 tile. A workgroup of nthr lanes covers rt = RPL * nthr / tpr rows:
+// lane (lane_row, kl) handles rows lane_row + j * nthr / tpr, j < RPL, and
+// chunks kl, kl + tpr, ... (< IMAX per row) of each. x is staged once per
+// workgroup; its loads are issued before the weight loads so that the LDS
+// staging and the barrier do not wait for the weights (vector loads complete
+// in issue order). Every load is unconditional (lanes without work read out
+// of range and get zeros), so the number of loads in flight is static and
+// each chunk is consumed as soon as its own loads have landed.
+template <int NK, int G, int RPL, int IMAX, int XMAX>
 __device__ __forceinline__ void tile_b1(const KParams& p, u32x4* xs, int row0, int nr, int sz_base) {
   constexpr int CPC = 128 / NK, BPC = CPC / 8, LSTRIDE = BPC + 1;
   constexpr int SPC = (G >= CPC) ? 1 : CPC / G;
   constexpr int SHARE = (G > CPC) ? G / CPC : 1;
   const int tid = threadIdx.x, nthr = blockDim.x;
-  const Role ro = make_role(p, tid, nr);
-  const int64_t slot0 = (int64_t)row0 * p.C;
+  const int tl = p.tpr_log2, TPR = 1 << tl;
+  const int lane_row = tid >> tl, kl = tid & (TPR - 1);
+  const int rows_per_pass = nthr >> tl;
+  const int C = p.C;
+  const int I = (C + TPR - 1) >> tl;
+  const int rem = C - (I - 1) * TPR;
   Consts k;
   k.magic = 0x64006400u;
   k.sel_or = NK == 2 ? 0x04040000u : 0x04000400u;
 
-  // 1. x loads (16 bytes = 8 columns each); surplus lanes re-load the last
-  //    block. The planes are formed unconditionally so that the loads stay
-  //    ahead of the weight loads.
+  // per-workgroup buffer windows
+  const uint32_t tile_slots = (uint32_t)nr * (uint32_t)C;
+  const int64_t slot0 = (int64_t)row0 * C;
+  const auto rx = make_rsrc(p.x, (uint32_t)p.K * 2u);
+  const auto rv = make_rsrc(p.vals + slot0, tile_slots * 16u);
+  const auto ro = make_rsrc(p.offs + slot0, tile_slots * 8u);
+  const auto rs = make_rsrc(p.sz + sz_base, tile_slots * (uint32_t)CPC / (uint32_t)G * 4u);
+  const auto rp = make_rsrc(p.perm + row0, (uint32_t)nr * 4u);
+
+  // 1. x loads (16 bytes = 8 columns each)
   const int nblk = p.K >> 3;
   u32x4 xv[XMAX];
 #pragma unroll
-  for (int j = 0; j < XMAX; ++j) {
-    const int m = tid + j * nthr;
-    xv[j] = p.x[m < nblk ? m : nblk - 1];
-  }
+  for (int j = 0; j < XMAX; ++j) xv[j] = bload4(rx, (uint32_t)(tid + j * nthr) * 16u);
   __builtin_amdgcn_sched_barrier(0);
-  // 2. weight loads; lanes without a chunk load the row's first chunk
-  const int rr = ro.active ? ro.r : 0;
-  const int yrow = p.perm[row0 + rr];
-  u32x4 v[MAXCH];
-  u32x2 o[MAXCH];
-  uint32_t s[MAXCH][SPC];
+  // 2. row indices and weight loads
+  uint32_t yrow[RPL];
+  bool has[RPL][IMAX];
+  u32x4 v[RPL][IMAX];
+  u32x2 o[RPL][IMAX];
+  uint32_t s[RPL][IMAX][SPC];
 #pragma unroll
-  for (int i = 0; i < MAXCH; ++i) {
-    const int ii = (i < ro.nch) ? i : 0;
-    const int kk = (i < ro.nch) ? ro.kl : 0;
-    const int cnt = (ii == ro.I - 1) ? ro.rem : ro.TPR;
-    load_chunk<SPC, SHARE>(p, slot0, ii * nr * ro.TPR + rr * cnt + kk, sz_base, v[i], o[i], s[i]);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // 3. x planes into LDS
+  for (int j = 0; j < RPL; ++j) {
+    const int r = lane_row + j * rows_per_pass;
+    const bool row_ok = r < nr;
+    yrow[j] = bload1(rp, row_ok ? (uint32_t)r * 4u : kOutOfRange);
 #pragma unroll
-  for (int j = 0; j < XMAX; ++j) {
-    const int m = tid + j * nthr;
-    u32x4 pl;
-    pl.x = perm_b32(xv[j].y, xv[j].x, 0x06040200u);  // low bytes of columns 0..3
-    pl.y = perm_b32(xv[j].w, xv[j].z, 0x06040200u);  // low bytes of columns 4..7
-    pl.z = perm_b32(xv[j].y, xv[j].x, 0x07050301u);  // high bytes of columns 0..3
-    pl.w = perm_b32(xv[j].w, xv[j].z, 0x07050301u);  // high bytes of columns 4..7
-    if (m < nblk) xs[(m / BPC) * LSTRIDE + (m % BPC)] = pl;
-  }
-  __syncthreads();
-  // 4. compute
-  float tot[1] = {0.0f};
-#pragma unroll
-  for (int i = 0; i < MAXCH; ++i) {
-    if (i < ro.nch) {
-      const u32x4* xc = xs + (i * ro.TPR + ro.kl) * LSTRIDE;
-      chunk_compute<NK, G, 1, SPC>(v[i], o[i], s[i], xc, 0, 1, tot, k);
+    for (int i = 0; i < IMAX; ++i) {
+      const bool ok = row_ok && (i < I - 1 || (i == I - 1 && kl < rem));
+      has[j][i] = ok;
+      const int cnt = (i == I - 1) ? rem : TPR;
+      const uint32_t s_rel = (uint32_t)(i * nr * TPR + r * cnt + kl);
+      v[j][i] = bload4<kStream>(rv, ok ? s_rel * 16u : kOutOfRange);
+      o[j][i] = bload2<kStream>(ro, ok ? s_rel * 8u : kOutOfRange);
+      const uint32_t soff = ok ? (SPC > 1 ? s_rel * SPC : s_rel / SHARE) * 4u : kOutOfRange;
+      if constexpr (SPC == 4) {
+        const u32x4 w = bload4<kStream>(rs, soff);
+        s[j][i][0] = w.x; s[j][i][1] = w.y; s[j][i][2] = w.z; s[j][i][3] = w.w;
+      } else if constexpr (SPC == 2) {
+        const u32x2 w = bload2<kStream>(rs, soff);
+        s[j][i][0] = w.x; s[j][i][1] = w.y;
+      } else {
+        s[j][i][0] = bload1<kStream>(rs, soff);
+      }
     }
   }
-  const float a = row_reduce(tot[0], p.tpr_log2);
-  if (ro.active && ro.kl == ro.TPR - 1) p.y[yrow] = __builtin_bit_cast(uint16_t, (_Float16)a);
+  __builtin_amdgcn_sched_barrier(0);
+  // 3. x planes into LDS (low bytes of 8 columns, then their high bytes)
+#pragma unroll
+  for (int j = 0; j < XMAX; ++j) {
+    const int m = tid + j * nthr;
+    if (XMAX == 1 || m < nblk) {
+      u32x4 pl;
+      pl.x = perm_b32(xv[j].y, xv[j].x, 0x06040200u);
+      pl.y = perm_b32(xv[j].w, xv[j].z, 0x06040200u);
+      pl.z = perm_b32(xv[j].y, xv[j].x, 0x07050301u);
+      pl.w = perm_b32(xv[j].w, xv[j].z, 0x07050301u);
+      xs[(m / BPC) * LSTRIDE + (m % BPC)] = pl;
+    }
+  }
+  __syncthreads();
+  // 4. compute row by row, chunk by chunk as the loads land
+#pragma unroll
+  for (int j = 0; j < RPL; ++j) {
+    const int r = lane_row + j * rows_per_pass;
+    float tot[1] = {0.0f};
+#pragma unroll
+    for (int i = 0; i < IMAX; ++i) {
+      if (has[j][i]) {   // the LDS beyond the last chunk's columns holds no x
+        const u32x4* xc = xs + (i * TPR + kl) * LSTRIDE;
+        chunk_compute<NK, G, 1, SPC>(v[j][i], o[j][i], s[j][i], xc, 0, 1, tot, k);
+      }
+    }
+    const float a = row_reduce(tot[0], tl);
+    if (r < nr && kl == TPR - 1) p.y[yrow[j]] = __builtin_bit_cast(uint16_t, (_Float16)a);
+  }
 }
 
 // Batch-1 kernel: one workgroup per tile.
-template <int NK, int MAXCH, int XMAX, int WGMAX>
-__global__ __launch_bounds__(WGMAX) void sgemv_b1_kernel(KParams p) {
+template <int NK, int RPL, int IMAX, int XMAX>
+__global__ __launch_bounds__(256) void sgemv_b1_kernel(KParams p) {
   extern __shared__ u32x4 xs[];
+  if ((int)blockIdx.x >= p.cls_tile[4]) return;   // no such tile (uniform per workgroup)
   const TileGeo t = tile_geo(p, blockIdx.x);
   switch (t.g) {
-    case 32: tile_b1<NK, 32, MAXCH, XMAX>(p, xs, t.row0, t.nr, t.sz_base); break;
-    case 64: tile_b1<NK, 64, MAXCH, XMAX>(p, xs, t.row0, t.nr, t.sz_base); break;
-    case 128: tile_b1<NK, 128, MAXCH, XMAX>(p, xs, t.row0, t.nr, t.sz_base); break;
-    default: tile_b1<NK, 256, MAXCH, XMAX>(p, xs, t.row0, t.nr, t.sz_base); break;
+    case 32: tile_b1<NK, 32, RPL, IMAX, XMAX>(p, xs, t.row0, t.nr, t.sz_base); break;
+    case 64: tile_b1<NK, 64, RPL, IMAX, XMAX>(p, xs, t.row0, t.nr, t.sz_base); break;
+    case 128: tile_b1<NK, 128, RPL, IMAX, XMAX>(p, xs, t.row0, t.nr, t.sz_base); break;
+    default: tile_b1<NK, 256, RPL, IMAX, XMAX>(p, xs, t.row0, t.nr, t.sz_base); break;
   }
 }
 
@@ -417,6 +475,7 @@ template <int NK>
 __global__ __launch_bounds__(256) void sgemv_bn_kernel(KParams p) {
   extern __shared__ u32x4 xs[];
   const int pass = blockIdx.x & ((1 << p.pass_log2) - 1);
+  if ((int)(blockIdx.x >> p.pass_log2) >= p.cls_tile[4]) return;   // no such tile
   const TileGeo t = tile_geo(p, blockIdx.x >> p.pass_log2);
   const int row0 = t.row0, nr = t.nr, g = t.g, sz_base = t.sz_base;
   const int vt = threadIdx.x + 256 * pass;

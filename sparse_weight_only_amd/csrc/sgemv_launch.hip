@@ -39,27 +39,61 @@ bool desc_consistent(const sgemv_desc* d) {
 
 }  // namespace
 
-extern "C" int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* x_dev, void* y_dev,
-                         int32_t B, void* hip_stream) {
-  if (!d || !blob_dev || !x_dev || !y_dev) return SGEMV_EINVAL;
+namespace {
+
+// What sgemv_run launches for a descriptor and batch: pure host arithmetic.
+int make_plan(const sgemv_desc* d, int32_t B, sgemv_plan_t* pl) {
+  if (!d || !pl) return SGEMV_EINVAL;
   if (B < 1 || B > 16) return SGEMV_EINVAL;
   if (!desc_consistent(d)) return SGEMV_ESIZE;
-  if (((uintptr_t)blob_dev % 256) || ((uintptr_t)x_dev % 16) || ((uintptr_t)y_dev % 2)) return SGEMV_EALIGN;
   const int cpc = cols_per_chunk(d->nk);
   const int32_t C = d->K * d->nk / 128;
-  const int32_t I = (C + d->tpr - 1) / d->tpr;
+  const Geometry geo = geometry(d->K, C, d->tpr, d->rt);
   const int wg_layout = d->rt * d->tpr;
-  const int wg = (B == 1) ? wg_layout : std::min(wg_layout, sgemv_dev::kBatchedThreads);
-  const int pass_log2 = ilog2(wg_layout / wg);
-  // x columns staged per phase: whole iterations of all lanes, B vectors
+  sgemv_plan_t q;
+  memset(&q, 0, sizeof q);
+  q.batched = B > 1;
+  if (B == 1) {
+    // one workgroup per tile; each lane owns geo.rpl rows of the tile
+    q.block = geo.wg;
+    q.pass_log2 = 0;
+    q.rows_per_lane = geo.rpl;
+  } else {
+    // 256-lane workgroups; a tile with more (row, lane) slots is split in passes
+    q.block = std::min(wg_layout, sgemv_dev::kBatchedThreads);
+    q.pass_log2 = ilog2(wg_layout / q.block);
+    q.rows_per_lane = 1;
+  }
+  q.grid = (int64_t)d->n_tiles << q.pass_log2;
+  q.chunks_per_row_lane = geo.iters;
+  // x columns staged per phase: whole chunk iterations of all lanes, for up to
+  // 4 batch vectors at a time
   const int bstage = B == 1 ? 1 : std::min<int>(B, sgemv_dev::kBatchGroup);
   const int64_t per_iter = (int64_t)bstage * d->tpr * (cpc / 8 + 1) * 16;
   const int64_t budget = (B == 1) ? 160 * 1024 : 65536;   // batch 1 stages all of x at once
-  int32_t pi = I;
+  int32_t pi = geo.iters;
   while (pi > 1 && per_iter * pi > budget) --pi;
-  const int64_t lds = per_iter * pi;
-  if (lds > 160 * 1024) return SGEMV_ESIZE;
-  if (B == 1 && pi != I) return SGEMV_ESIZE;   // the batch-1 kernel stages x once
+  q.lds_bytes = per_iter * pi;
+  q.phase_iters = pi;
+  if (q.lds_bytes > 160 * 1024) return SGEMV_ESIZE;
+  if (B == 1 && pi != geo.iters) return SGEMV_ESIZE;
+  *pl = q;
+  return SGEMV_OK;
+}
+
+}  // namespace
+
+extern "C" int sgemv_plan(const sgemv_desc* d, int32_t B, sgemv_plan_t* out) { return make_plan(d, B, out); }
+
+extern "C" int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* x_dev, void* y_dev,
+                         int32_t B, void* hip_stream) {
+  if (!d || !blob_dev || !x_dev || !y_dev) return SGEMV_EINVAL;
+  sgemv_plan_t pl;
+  const int rc = make_plan(d, B, &pl);
+  if (rc) return rc;
+  if (((uintptr_t)blob_dev % 256) || ((uintptr_t)x_dev % 16) || ((uintptr_t)y_dev % 2)) return SGEMV_EALIGN;
+  const int32_t C = d->K * d->nk / 128;
+  const Geometry geo = geometry(d->K, C, d->tpr, d->rt);
   const uint8_t* blob = (const uint8_t*)blob_dev;
   KParams p;
   p.tiles = (const int32_t*)(blob + d->off_tiles);
@@ -71,8 +105,8 @@ extern "C" int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* 
   p.y = (uint16_t*)y_dev;
   p.N = d->N; p.K = d->K; p.C = C; p.B = B;
   p.tpr_log2 = ilog2(d->tpr);
-  p.phase_iters = pi;
-  p.pass_log2 = pass_log2;
+  p.phase_iters = pl.phase_iters;
+  p.pass_log2 = pl.pass_log2;
   p.rt = d->rt;
   {
     int32_t t = 0, r = 0, z = 0;
@@ -84,19 +118,13 @@ extern "C" int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* 
     }
     p.cls_tile[4] = t; p.cls_row[4] = r;
   }
-  KernelFn fn;
-  if (B == 1) {
-    const int per_lane = (d->K / 8 + wg - 1) / wg;
-    if (per_lane > 8) return SGEMV_ESIZE;
-    fn = sgemv_dev::get_b1(d->nk, sgemv_dev::maxch_bucket(I), sgemv_dev::xmax_bucket(per_lane));
-  }
-  else fn = sgemv_dev::get_bn(d->nk);
-  if (lds > 65536) {
-    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+  KernelFn fn = (B == 1) ? sgemv_dev::get_b1(d->nk, geo.rpl, geo.imax, geo.xmax) : sgemv_dev::get_bn(d->nk);
+  if (!fn) return SGEMV_ESIZE;
+  if (pl.lds_bytes > 65536) {
+    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds_bytes) != hipSuccess)
       return SGEMV_EHIP;
   }
-  hipLaunchKernelGGL(fn, dim3((uint32_t)d->n_tiles << pass_log2), dim3(wg), (uint32_t)lds,
-                     (hipStream_t)hip_stream, p);
+  hipLaunchKernelGGL(fn, dim3((uint32_t)pl.grid), dim3(pl.block), (uint32_t)pl.lds_bytes, (hipStream_t)hip_stream, p);
   if (hipGetLastError() != hipSuccess) return SGEMV_EHIP;
   return SGEMV_OK;
 }

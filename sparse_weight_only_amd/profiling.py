@@ -1,0 +1,121 @@
+"""Summaries of rocprofv3 runs of ``bench.py`` for the ``profiles/`` folder.
+
+Usage (after the rocprofv3 runs named in each summary's header):
+
+    python -m sparse_weight_only_amd.profiling stats  <kernel_stats.csv> <out.txt> "<command>"
+    python -m sparse_weight_only_amd.profiling traffic <fetch counter_collection.csv>
+                     <write counter_collection.csv> <out.json> "<fetch command>" "<write command>"
+
+``traffic`` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the
+same counters read for the 64 MiB reference copy that ``bench.py`` performs
+at start-up (64 MiB read, 64 MiB written), and records them per workload
+layer together with a hash of the kernel sources, so that ``bench.py``
+reports HBM traffic only while the kernels are unchanged.
+"""
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+REF_KIB = 64 * 1024          # the reference copy: 64 MiB each way
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(HERE, "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    return name.replace("(anonymous namespace)::", "").replace("sgemv_dev::", "").split("(")[0]
+
+
+def stats_summary(stats_csv: str, out_txt: str, command: str) -> None:
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel statistics (kernel sources {kernel_source_hash()})",
+             f"# command: {command}", "",
+             f"{'kernel':62s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for r in rows:
+        lines.append(f"{short_name(r['Name'])[:62]:62s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.3f} "
+                     f"{float(r['MinNs']) / 1e3:9.3f} {float(r['MaxNs']) / 1e3:9.3f} {float(r['Percentage']):6.2f}")
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _counter_medians(path: str, counter: str):
+    by = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        by[(r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"]))].append(float(r["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in by.items()}
+
+
+def _reference(med: dict) -> float:
+    """Counter value of the 64 MiB reference copy (the largest copy dispatch)."""
+    cands = [(v, k) for k, v in med.items() if "copyBuffer" in k[0] or "elementwise" in k[0] and "copy" in k[0].lower()]
+    cands = [c for c in cands if c[0] > REF_KIB / 8]
+    if not cands:
+        raise RuntimeError("reference copy not found in the counter run")
+    return max(cands)[0]
+
+
+def traffic_summary(fetch_csv: str, write_csv: str, out_json: str, fetch_cmd: str, write_cmd: str,
+                    layer_kernels: dict) -> dict:
+    """layer_kernels: layer name -> (kernel name substring, grid size in lanes)."""
+    fm = _counter_medians(fetch_csv, "FETCH_SIZE")
+    wm = _counter_medians(write_csv, "WRITE_SIZE")
+    f_scale = REF_KIB / _reference(fm)
+    w_scale = REF_KIB / _reference(wm)
+    out = {"kernel_source_hash": kernel_source_hash(), "fetch_scale": round(f_scale, 4),
+           "write_scale": round(w_scale, 4), "fetch_command": fetch_cmd, "write_command": write_cmd,
+           "hbm_bytes_per_launch": {}, "raw_kib_per_dispatch": {}}
+    for layer, (kname, grid) in layer_kernels.items():
+        fk = [v for k, v in fm.items() if kname in k[0] and k[1] == grid]
+        wk = [v for k, v in wm.items() if kname in k[0] and k[1] == grid]
+        if len(fk) != 1 or len(wk) != 1:
+            continue
+        out["raw_kib_per_dispatch"][layer] = {"FETCH_SIZE": fk[0], "WRITE_SIZE": wk[0]}
+        out["hbm_bytes_per_launch"][layer] = int(round((fk[0] * f_scale + wk[0] * w_scale) * 1024))
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
+def _bench_layer_kernels() -> dict:
+    """Kernel name and grid of each bench layer, from the library's own launch plan."""
+    sys.path.insert(0, os.path.dirname(HERE))
+    import numpy as np
+    import synth
+    import sparse_weight_only_amd as sg
+    res = {}
+    for L in synth.cfg3():
+        W = L.W()
+        gs = sg.select_groups(W, L.nk, L.Xcal(synth.CALIB_T), synth.FRAC_FINE, synth.G_FINE, synth.G_COARSE)
+        d = sg.describe(L.N, L.K, L.nk, gs)
+        pl = sg.plan(d, 1)
+        C = L.K * L.nk // 128
+        iters = -(-C // d.tpr)
+        imax = 1 if iters <= 1 else 2 if iters <= 2 else 4 if iters <= 4 else 8
+        xmax = 2 if -(-(L.K // 8) // pl.block) <= 2 else 8
+        name = f"sgemv_b1_kernel<{L.nk}, {pl.rows_per_lane}, {imax}, {xmax}>"
+        res[L.name] = (name, int(pl.grid * pl.block))
+    return res
+
+
+if __name__ == "__main__":
+    if len(sys.argv) >= 5 and sys.argv[1] == "stats":
+        stats_summary(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif len(sys.argv) >= 7 and sys.argv[1] == "traffic":
+        print(json.dumps(traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6],
+                                         _bench_layer_kernels()), indent=1))
+    else:
+        print(__doc__)
+        sys.exit(2)

@@ -47,6 +47,17 @@ class Desc(ctypes.Structure):
         return {f: (list(getattr(self, f)) if f == "class_rows" else getattr(self, f)) for f, _ in self._fields_}
 
 
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int64), ("block", ctypes.c_int32),
+        ("pass_log2", ctypes.c_int32), ("rows_per_lane", ctypes.c_int32),
+        ("chunks_per_row_lane", ctypes.c_int32), ("phase_iters", ctypes.c_int32), ("batched", ctypes.c_int32),
+    ]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
 def lib_path() -> str:
     return _LIB_PATH
 
@@ -66,9 +77,10 @@ def lib():
         L.sgemv_pack.argtypes = [P, i32, i32, i32, P, P, P, P, P, P, P]
         L.sgemv_layout.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P, P]
         L.sgemv_run.argtypes = [ctypes.POINTER(Desc), P, P, P, i32, P]
+        L.sgemv_plan.argtypes = [ctypes.POINTER(Desc), i32, ctypes.POINTER(Plan)]
         L.sgemv_strerror.argtypes = [ctypes.c_int]
         L.sgemv_strerror.restype = ctypes.c_char_p
-        for f in ("sgemv_describe", "sgemv_select_groups", "sgemv_pack", "sgemv_layout", "sgemv_run"):
+        for f in ("sgemv_describe", "sgemv_select_groups", "sgemv_pack", "sgemv_layout", "sgemv_run", "sgemv_plan"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -149,6 +161,13 @@ def run(desc: Desc, blob_dev: int, x_dev: int, y_dev: int, B: int, stream: int =
     """Enqueue y = W' x on ``stream`` (raw device pointers as ints)."""
     _check(lib().sgemv_run(ctypes.byref(desc), ctypes.c_void_p(blob_dev), ctypes.c_void_p(x_dev),
                            ctypes.c_void_p(y_dev), B, ctypes.c_void_p(stream)), "sgemv_run")
+
+
+def plan(desc: Desc, B: int) -> Plan:
+    """The launch sgemv_run would make for (desc, B); no GPU needed."""
+    pl = Plan()
+    _check(lib().sgemv_plan(ctypes.byref(desc), B, ctypes.byref(pl)), "sgemv_plan")
+    return pl
 
 
 def algorithmic_bytes(desc: Desc, B: int) -> int:

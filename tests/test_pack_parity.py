@@ -160,3 +160,35 @@ def test_error_paths():
     canon = sg.pack(np.zeros((8, 256), np.float16), 2, g)
     with pytest.raises(sg.SgemvError):
         sg.layout(bad, canon)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_launch_plan_covers_each_tile_once(seed):
+    """sgemv_plan (host arithmetic only): one workgroup per tile at batch 1, whole passes of
+    256 lanes per tile for beam batches; the LDS holds every staged x column of a phase."""
+    rng = np.random.default_rng(seed)
+    for _ in range(25):
+        nk = int(rng.choice([1, 2]))
+        K = int(rng.choice([256, 512, 768, 1024, 1280, 2816, 4096, 11008]))
+        N = int(rng.integers(1, 700))
+        gs = rng.choice([g for g in (32, 64, 128) if K % g == 0], N).astype(np.int32)
+        C = K * nk // 128
+        tpr = int(rng.choice([4, 8, 16, 32, 64]))
+        rt = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128, 256])) if seed else 0
+        try:
+            d = sg.describe(N, K, nk, gs, rt, tpr if rt else 0)
+        except sg.SgemvError:
+            continue
+        cpc = 128 // nk
+        for B in (1, 3, 16):
+            pl = sg.plan(d, B)
+            slots = d.rt * d.tpr
+            if B == 1:
+                assert pl.grid == d.n_tiles and pl.pass_log2 == 0 and not pl.batched
+                assert pl.block * pl.rows_per_lane == slots and pl.block <= 256
+                assert pl.lds_bytes >= C * (cpc // 8 + 1) * 16          # all of x, with pads
+            else:
+                assert pl.batched and pl.grid == d.n_tiles << pl.pass_log2
+                assert pl.block << pl.pass_log2 == slots and pl.block <= 256
+            assert pl.lds_bytes <= 160 * 1024
+            assert pl.chunks_per_row_lane == -(-C // d.tpr)
