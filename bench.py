@@ -47,8 +47,6 @@ def parse():
     ap.add_argument("--layer-calls", type=int, default=400, help="launches per per-layer timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
-    ap.add_argument("--rt", type=int, default=0)
-    ap.add_argument("--tpr", type=int, default=0)
     return ap.parse_args()
 
 
@@ -138,7 +136,7 @@ def main():
         W = L.W()
         gs = sg.select_groups(W, L.nk, L.Xcal(synth.CALIB_T), synth.FRAC_FINE, synth.G_FINE, synth.G_COARSE)
         canon = sg.pack(W, L.nk, gs)
-        desc = sg.describe(L.N, L.K, L.nk, gs, args.rt, args.tpr)
+        desc = sg.describe(L.N, L.K, L.nk, gs)
         blob = sg.layout(desc, canon)
         nbytes = sg.algorithmic_bytes(desc, 1)
         X = L.X(1)
@@ -219,10 +217,11 @@ def main():
 
         ms_call = timed(body_layer, calls_per_graph, 4, 1)
         us = ms_call * 1e3
+        pl = sg.plan(l["desc"], 1)
         per_layer[l["L"].name] = {"us_per_call": round(us, 3), "bytes": l["bytes"],
                                   "GBps": round(l["bytes"] / (us * 1e-6) / 1e9, 1),
                                   "pct_hbm_peak": round(100 * l["bytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
-                                  "rt": l["desc"].rt, "tpr": l["desc"].tpr, "n_tiles": l["desc"].n_tiles}
+                                  "grid": pl.grid, "waves": pl.waves, "chunks_per_wave": pl.chunks_per_wave}
     # dominant kernel: the layer with the largest time per step
     dom = max(per_layer, key=lambda k: per_layer[k]["us_per_call"])
     d = per_layer[dom]

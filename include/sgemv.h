@@ -43,41 +43,35 @@ enum {
 /* Plain-data description of one packed layer. Filled by sgemv_describe and
  * passed back by pointer; the caller may copy it freely. */
 typedef struct sgemv_desc {
-  int32_t N, K;          /* output rows, input columns (K % 256 == 0)                */
-  int32_t nk;            /* kept elements per group of 4 along K: 2 (2:4) or 1 (1:4) */
-  int32_t rt;            /* kernel layout: rows per tile (one workgroup per tile)    */
-  int32_t tpr;           /* kernel layout: threads per row, power of two in [4, 64]  */
-  int32_t n_tiles;       /* tiles = workgroups launched by sgemv_run                 */
-  int32_t g_min, g_max;  /* smallest and largest group size present                  */
+  int32_t N, K;          /* output rows, input columns (K % 256 == 0)                  */
+  int32_t nk;            /* kept elements per group of 4 along K: 2 (2:4) or 1 (1:4)   */
+  int32_t n_blocks;      /* row blocks of 16 rows (rows sorted by group size)          */
+  int32_t chunks;        /* column chunks of 256 dense columns per row: K / 256        */
+  int32_t g_min, g_max;  /* smallest and largest group size present                    */
   int32_t class_rows[4]; /* rows with group size 32, 64, 128, 256 (sorted in that order) */
-  int32_t reserved;      /* zero                                                     */
-  int64_t kept;          /* N*K*nk/4 kept elements                                   */
-  int64_t vals_bytes;    /* canonical code array: kept/2 bytes (one nibble each)     */
-  int64_t offs_bytes;    /* canonical offset array: kept/4 bytes (2 bits each)       */
-  int64_t n_groups;      /* sum_n K/g_n: one FP16 scale and one FP16 zero each       */
-  int64_t off_tiles;     /* byte offsets of the blob sections (256-byte aligned)     */
-  int64_t off_perm;
-  int64_t off_vals;
+  int32_t reserved;      /* zero                                                       */
+  int64_t kept;          /* N*K*nk/4 kept elements                                     */
+  int64_t vals_bytes;    /* canonical code array: kept/2 bytes (one nibble each)       */
+  int64_t offs_bytes;    /* canonical offset array: kept/4 bytes (2 bits each)         */
+  int64_t n_groups;      /* sum_n K/g_n: one FP16 scale and one FP16 zero each         */
+  int64_t off_codes;     /* byte offsets of the blob sections (256-byte aligned)       */
   int64_t off_offs;
+  int64_t off_perm;
   int64_t off_sz;
-  int64_t blob_bytes;    /* total size of the kernel-layout blob                     */
+  int64_t blob_bytes;    /* total size of the kernel-layout blob                       */
 } sgemv_desc;
 
 /* sgemv_describe - validate a layer shape and fill its descriptor.
- *   N, K         : rows and columns; N >= 1, K >= 256, K % 256 == 0, N*K*nk/4 < 2^31.
+ *   N, K         : rows and columns; N >= 1, K >= 256, K % 256 == 0, K <= 32768,
+ *                  and the blob must stay below 2^31 bytes.
  *   nk           : 2 for 2:4 or 1 for 1:4 (P1 §3.2 "Sparsification").
  *   group_size   : host int32[N], group size of each row in dense columns; each
- *                  in {32, 64, 128, 256} and dividing K (P1 §3.2 "Adaptive group
- *                  quantization": finer groups for sensitive channels).
- *   rt, tpr      : kernel layout; 0 and 0 pick defaults for this shape. Otherwise
- *                  tpr in {4,8,16,32,64}; rt*tpr a power of two in [64, 1024], run
- *                  by workgroups of min(256, rt*tpr) lanes owning rt*tpr/256 rows
- *                  each; at most 8 chunks (32 kept elements each) of a row per
- *                  lane and 8 per lane in all; at most 8 16-byte x blocks per lane.
+ *                  in {32, 64, 128, 256} (P1 §3.2 "Adaptive group quantization":
+ *                  finer groups for sensitive channels).
  *   out          : filled on success.
- * Errors: EINVAL for bad arguments, ESIZE if the layout constraints cannot be met. */
+ * Errors: EINVAL for bad arguments, ESIZE beyond the supported sizes. */
 int sgemv_describe(int32_t N, int32_t K, int32_t nk, const int32_t* group_size,
-                   int32_t rt, int32_t tpr, sgemv_desc* out);
+                   sgemv_desc* out);
 
 /* sgemv_select_groups - adaptive group size per output channel (P1 §3.2
  * "Adaptive group quantization"; sensitivity from the first term of eq. (3)).
@@ -114,13 +108,27 @@ int sgemv_pack(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
                uint16_t* scale, uint16_t* zero, int32_t* gptr, int32_t* rowptr);
 
 /* sgemv_layout - canonical arrays -> kernel-layout blob (host). The blob holds
- * the same bits reordered for coalesced 16/8/4-byte loads: tile table, row
- * permutation (rows sorted by group size), codes, offsets and packed
- * scale|zero<<16 words; the exact rules are written out with the oracle's
- * layout module and in the design notes. Group sizes are taken from gptr.
+ * the same bits reordered for the matrix-core kernel (no duplication; zero
+ * padding only for the rows of a last, partial row block):
+ *  - rows sorted by group size (ascending, stable); row block b = sorted rows
+ *    16b..16b+15; a piece = one row's kept elements in 64 dense columns;
+ *  - codes [blocks][chunks][64 lanes][2*nk*4 bytes] and offsets
+ *    [blocks][chunks][64 lanes][nk*4 bytes]: lane r + 16q of record (b, c)
+ *    holds the piece of sorted row 16b + r in columns 256c + 64q .. +63, with
+ *    a fixed nibble order inside each code dword and, at 1:4, a fixed 2-bit
+ *    order inside the offset dword;
+ *  - perm int32[16*blocks]: original row of each sorted row, -1 for padding;
+ *  - scale|zero<<16 words in records (b, c), each listing the rows of block b
+ *    in order with their 256/g words of chunk c.
+ * The exact bit positions are listed with the layout builder (host_layout.cpp)
+ * and the oracle's layout module. Group sizes are taken from gptr.
  *   d        : descriptor from sgemv_describe for the same group sizes.
  *   blob     : host buffer of d->blob_bytes bytes, fully written.
- * Errors: EINVAL (NULL, gptr inconsistent with d), ESIZE. */
+ * The kernel holds each weight as the FP16 value (code - zero) * scale, rounded
+ * once; a layer where that value rounds beyond the FP16 range (|value| >=
+ * 65520, possible only for groups reaching within 2^-11 of the FP16 maximum)
+ * is rejected with EINVAL.
+ * Errors: EINVAL (NULL, gptr inconsistent with d, FP16 range), ESIZE. */
 int sgemv_layout(const sgemv_desc* d, const uint8_t* vals, const uint8_t* offs,
                  const uint16_t* scale, const uint16_t* zero, const int32_t* gptr,
                  void* blob);
@@ -133,6 +141,11 @@ int sgemv_layout(const sgemv_desc* d, const uint8_t* vals, const uint8_t* offs,
  *   y_dev    : device FP16 [B][N] row-major, 2-byte aligned; fully overwritten.
  *   B        : batch (beam width), 1..16.
  *   hip_stream : hipStream_t to enqueue on (NULL = default stream).
+ * Numerics: each weight enters as FP16 (code - zero) * scale (one rounding,
+ * relative error <= 2^-11), products and sums in FP32, y rounded to FP16;
+ * |y - W'x| <= (2^-11 + n 2^-24) sum_k |W'[n][k] x[k]| + 2^-11 |y| for n
+ * kept elements per row. Non-finite x gives non-finite rows, as the dense
+ * product does.
  * Enqueues one kernel and returns without synchronising. x and y must not
  * overlap the blob or each other. Deterministic: the same inputs give the
  * same bits on every call. Errors: EINVAL, ESIZE, EALIGN (host checks), EHIP. */
@@ -141,14 +154,15 @@ int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* x_dev,
 
 /* What sgemv_run enqueues for a layer and a batch (filled by sgemv_plan). */
 typedef struct sgemv_plan_t {
-  int64_t grid;                /* workgroups launched                                  */
-  int64_t lds_bytes;           /* dynamic LDS per workgroup (staged x planes)          */
-  int32_t block;               /* lanes per workgroup                                  */
-  int32_t pass_log2;           /* log2 of workgroups per tile (beam-batch kernel)      */
-  int32_t rows_per_lane;       /* rows each lane accumulates (batch-1 kernel)          */
-  int32_t chunks_per_row_lane; /* 32-element chunks of one row per lane                */
-  int32_t phase_iters;         /* chunk iterations whose x is staged at once           */
-  int32_t batched;             /* 1 if the beam-batch kernel runs, else 0              */
+  int64_t grid;            /* workgroups launched: one per row block                  */
+  int64_t lds_bytes;       /* dynamic LDS per workgroup (x slices and wave partials)  */
+  int32_t block;           /* lanes per workgroup: 64 * waves                         */
+  int32_t waves;           /* waves per workgroup; wave w owns column chunks           */
+                           /* [w * chunks_per_wave, (w + 1) * chunks_per_wave)        */
+  int32_t chunks_per_wave;
+  int32_t phase_chunks;    /* chunks whose x slice is staged in LDS at once           */
+  int32_t x_loads;         /* 16-byte x loads per lane and phase                      */
+  int32_t reserved;        /* zero                                                    */
 } sgemv_plan_t;
 
 /* sgemv_plan - describe the launch sgemv_run would make for (d, B) without

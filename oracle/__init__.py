@@ -32,8 +32,8 @@ Modules and what pins each one (tests under ``tests/test_oracle_*.py``):
                pinned by exact rational sums, math.fsum and unit vectors.
 
 Parity unpinned: nothing in this package. What the pages leave open (their
-own bit layout, their sensitivity measure, their kernel) is replaced by the
-readings listed in the repository's design notes; those readings are pinned,
-the pages' originals cannot be.
+own bit layout, their sensitivity measure, their kernel) is replaced by
+explicit readings, each stated with the function that takes it; those
+readings are pinned, the pages' originals cannot be.
 """
 from . import fp16, prune, groups, quant, pack, layout, gemv  # noqa: F401

@@ -1,212 +1,177 @@
 """Kernel layout: a documented permutation of the canonical 2bit-CSR arrays.
 
-The GPU kernel reads the same bits as the canonical arrays (no padding, no
-duplication), reordered so that every load is a coalesced 16-byte (values),
-8-byte (offsets) or 4-byte (scale+zero) access. This module builds that
-blob from the canonical arrays, element by element, from the rules below.
+Test infrastructure (see the package docstring). The GPU kernel reads the
+same bits as the canonical arrays, reordered for the 2-of-4 sparse
+matrix-core instruction (16 rows x 64 dense columns per instruction); this
+module builds that blob from the canonical arrays, element by element, from
+the rules below, and reads it back.
 
 Terms
-* chunk: 32 consecutive kept elements of a row (16 bytes of codes, 8 bytes of
-  offsets); it spans cpc = 128/nk dense columns (64 at 2:4, 128 at 1:4).
-  A row has C = K*nk/128 chunks.
-* row order: rows sorted by group size (smaller first), ascending row index
-  within a size (``perm[i]`` = original row of sorted position i).
-* tile: up to RT consecutive sorted rows of one group size. Within a tile,
-  TPR threads work on each row; chunk c of a row goes to k-lane c % TPR at
-  iteration c // TPR. There are I = ceil(C/TPR) iterations; all but the last
-  hold TPR chunks per row, the last holds rem = C - (I-1)*TPR.
-* slot: position of a chunk in the tile's streams,
-      slot = row0*C + i*nr*TPR + r*cnt_i + kl
-  with row0 the tile's first sorted row, nr its row count, r the row within
-  the tile, kl the k-lane and cnt_i the chunks per row of iteration i.
+* sorted rows: rows ordered by group size (smaller first), ascending row
+  index within a size; ``perm[i]`` = original row of sorted position i.
+* row block b: sorted rows 16b .. 16b+15; T = ceil(N / 16) blocks; rows past
+  N in the last block are padding.
+* column chunk c: dense columns 256c .. 256c+255; C = K / 256 chunks.
+* piece (i, c, q), q = 0..3: sorted row i, dense columns 256c + 64q .. +63;
+  it holds the row's kept elements e0 .. e0 + 16*nk - 1, e0 = 16*nk*(4c + q)
+  (an N:M row keeps exactly nk per 4 columns, so pieces are aligned).
+* record (b, c): 64 lanes; lane r + 16q holds piece (16b + r, c, q).
 
-Bits inside a chunk (element e = 0..31 of the chunk)
-* codes: 4 little-endian dwords; dword d holds elements 8d..8d+7, nibble k
-  (bits 4k..4k+3) holds element 8d + 2k for k < 4 and 8d + 2(k-4) + 1 for
-  k >= 4, so that masking 0x000F000F / 0x00F000F0 yields consecutive pairs;
-* offsets: 2 little-endian dwords; dword D holds elements 16D..16D+15,
-  element 16D + 4q + b at bits 8b + 2q, so that (dword >> 2q) & 0x03030303
-  gives the offsets of 4 consecutive elements in 4 bytes.
+Bits of a piece
+* codes (8*nk bytes): little-endian dwords of 8 consecutive elements; element
+  k (0..7) of a dword sits at nibble NIB[k], NIB = [0,4,1,5,2,6,3,7] at 2:4
+  and [0,1,4,5,2,3,6,7] at 1:4 (so that the masks 0x000F000F / 0x00F000F0
+  pick the pairs the kernel feeds into one matrix-core register);
+* offsets (4*nk bytes): at 2:4 the canonical 2-bit fields, element m at bits
+  2m of a little-endian 64-bit word (bytes unchanged); at 1:4 one dword with
+  element m at bit 16*((m//4) % 2) + (REAL if m//4 < 2 else DUMMY)[m % 4],
+  REAL = [0,4,10,14], DUMMY = [2,6,8,12].
 
-Scale/zero stream: one 32-bit entry per group, FP16 scale in the low half,
-FP16 zero in the high half. A chunk at slot s of a tile with group size g
-uses entries sz_base + (s*cpc)//g + j, j < max(1, cpc//g); chunks that share
-a group share its entry (consecutive slots, so the entry is stored once).
+Scale/zero: one 32-bit word per group, FP16 scale in the low half, FP16 zero
+in the high half; records (b, c) in (b, c) order, each listing the rows of
+block b in order, each row with its 256/g words of chunk c (its groups
+c*256/g .. (c+1)*256/g - 1). Padding rows have no words.
 
-Blob sections (each starting on a 256-byte boundary, in this order):
-tiles int32[n_tiles][4] = (row0, nr, g, sz_base); perm int32[N];
-codes (N*C*16 B); offsets (N*C*8 B); scale/zero (n_groups*4 B).
+Blob sections (each starting on a 256-byte boundary, in this order): codes
+[T][C][64][8*nk]; offsets [T][C][64][4*nk]; perm int32[16*T] (-1 for
+padding rows); scale/zero words, followed by 8 zero bytes.
 """
 import numpy as np
 
 from .pack import unpack_bytes
 
 ALIGN = 256
+NIB = {2: [0, 4, 1, 5, 2, 6, 3, 7], 1: [0, 1, 4, 5, 2, 3, 6, 7]}
+REAL = [0, 4, 10, 14]
+DUMMY = [2, 6, 8, 12]
 
 
 def _align(x: int) -> int:
     return (x + ALIGN - 1) // ALIGN * ALIGN
 
 
-def cols_per_chunk(nk: int) -> int:
-    return 128 // nk
-
-
 def row_order(group_size) -> np.ndarray:
     return np.argsort(np.asarray(group_size, dtype=np.int64), kind="stable").astype(np.int32)
 
 
-def tile_list(group_size, RT: int):
-    """[(row0, nr, g)] in sorted-row order, class by class."""
-    gs_sorted = np.asarray(group_size, dtype=np.int64)[row_order(group_size)]
-    tiles, i, N = [], 0, len(gs_sorted)
-    while i < N:
-        g = int(gs_sorted[i])
-        j = i
-        while j < N and gs_sorted[j] == g:
-            j += 1
-        for r0 in range(i, j, RT):
-            tiles.append((r0, min(RT, j - r0), g))
-        i = j
-    return tiles
+def off14_bit(m: int) -> int:
+    """Bit position of element m (0..15) of a 1:4 piece in its offset dword."""
+    t, e = divmod(m, 4)
+    return 16 * (t % 2) + (REAL if t < 2 else DUMMY)[e]
 
 
-def section_offsets(N: int, K: int, nk: int, n_tiles: int, n_groups: int) -> dict:
-    C = K * nk // 128
-    off = {"tiles": 0}
-    off["perm"] = _align(16 * n_tiles)
-    off["vals"] = _align(off["perm"] + 4 * N)
-    off["offs"] = _align(off["vals"] + 16 * N * C)
-    off["sz"] = _align(off["offs"] + 8 * N * C)
-    off["blob_bytes"] = _align(off["sz"] + 4 * n_groups)
+def section_offsets(N: int, K: int, nk: int, n_groups: int) -> dict:
+    T, C = -(-N // 16), K // 256
+    records = T * C * 64
+    off = {"codes": 0}
+    off["offs"] = _align(records * 8 * nk)
+    off["perm"] = _align(off["offs"] + records * 4 * nk)
+    off["sz"] = _align(off["perm"] + 4 * 16 * T)
+    off["blob_bytes"] = _align(off["sz"] + 4 * n_groups + 8)
     return off
 
 
-def _encode_codes(q32: np.ndarray) -> np.ndarray:
-    """[S, 32] codes -> [S, 16] bytes."""
-    S = q32.shape[0]
-    q = q32.astype(np.uint32).reshape(S, 4, 8)
-    src = [0, 2, 4, 6, 1, 3, 5, 7]            # element held by nibble k
-    dw = np.zeros((S, 4), dtype=np.uint32)
-    for k in range(8):
-        dw |= q[:, :, src[k]] << np.uint32(4 * k)
-    return dw.astype("<u4").view(np.uint8).reshape(S, 16)
-
-
-def _encode_offs(o32: np.ndarray) -> np.ndarray:
-    """[S, 32] offsets -> [S, 8] bytes."""
-    S = o32.shape[0]
-    o = o32.astype(np.uint32).reshape(S, 2, 4, 4)   # [S, D, q, b]
-    dw = np.zeros((S, 2), dtype=np.uint32)
-    for q in range(4):
-        for b in range(4):
-            dw |= o[:, :, q, b] << np.uint32(8 * b + 2 * q)
-    return dw.astype("<u4").view(np.uint8).reshape(S, 8)
-
-
-def build(canon: dict, RT: int, TPR: int) -> dict:
+def build(canon: dict) -> dict:
     """Canonical arrays -> kernel blob (bytes) plus its parts for inspection."""
     N, K, nk = canon["N"], canon["K"], canon["nk"]
     gs = np.asarray(canon["group_size"], dtype=np.int64)
-    cpc = cols_per_chunk(nk)
-    C = K * nk // 128
-    q, o = unpack_bytes(canon["vals"], canon["offs"])
-    scale = np.asarray(canon["scale"], dtype=np.uint32)
-    zero = np.asarray(canon["zero"], dtype=np.uint32)
-    sz_all = scale | (zero << np.uint32(16))
+    T, C, kpp = -(-N // 16), K // 256, 16 * nk
+    q, o = unpack_bytes(canon["vals"], canon["offs"])           # [N, K*nk/4] each
+    sz_all = (np.asarray(canon["scale"], dtype=np.uint32)
+              | (np.asarray(canon["zero"], dtype=np.uint32) << np.uint32(16)))
     gptr = np.asarray(canon["gptr"], dtype=np.int64)
     perm = row_order(gs)
-    tiles = tile_list(gs, RT)
-    vals_blob = np.zeros((N * C, 16), dtype=np.uint8)
-    offs_blob = np.zeros((N * C, 8), dtype=np.uint8)
+    # per sorted row: pieces [C, 4, kpp] of codes and offsets
+    qs = q[perm].astype(np.uint32).reshape(N, C, 4, kpp)
+    os_ = o[perm].astype(np.uint32).reshape(N, C, 4, kpp)
+    # codes: dwords of 8 elements, element k at nibble NIB[k]
+    qd = qs.reshape(N, C, 4, kpp // 8, 8)
+    cw = np.zeros((N, C, 4, kpp // 8), dtype=np.uint32)
+    for k in range(8):
+        cw |= qd[..., k] << np.uint32(4 * NIB[nk][k])
+    # offsets
+    if nk == 2:
+        od = os_.reshape(N, C, 4, 2, 16)
+        ow = np.zeros((N, C, 4, 2), dtype=np.uint32)
+        for m in range(16):
+            ow |= od[..., m] << np.uint32(2 * m)
+    else:
+        ow = np.zeros((N, C, 4, 1), dtype=np.uint32)
+        for m in range(16):
+            ow[..., 0] |= os_[..., m] << np.uint32(off14_bit(m))
+    # records (b, c): lane r + 16q <- piece (16b + r, c, q); padding rows stay zero
+    cwp = np.zeros((T * 16,) + cw.shape[1:], dtype=np.uint32)
+    owp = np.zeros((T * 16,) + ow.shape[1:], dtype=np.uint32)
+    cwp[:N], owp[:N] = cw, ow
+    codes = cwp.reshape(T, 16, C, 4, -1).transpose(0, 2, 3, 1, 4)     # [T, C, q, r, dw]
+    offs = owp.reshape(T, 16, C, 4, -1).transpose(0, 2, 3, 1, 4)
+    # scale/zero records
+    sz_words = []
+    for b in range(T):
+        rows = perm[16 * b: 16 * b + 16]
+        per_row = []
+        for n in rows:
+            g = int(gs[n])
+            per_row.append(sz_all[gptr[n]: gptr[n + 1]].reshape(C, 256 // g))
+        sz_words.append(np.concatenate(per_row, axis=1).reshape(-1))      # chunk-major
+    sz = np.concatenate(sz_words).astype(np.uint32)
     n_groups = int(gptr[N])
-    sz_blob = np.zeros(n_groups, dtype=np.uint32)
-    sz_filled = np.zeros(n_groups, dtype=bool)
-    tile_tab = np.zeros((len(tiles), 4), dtype=np.int32)
-    sz_base = 0
-    I = -(-C // TPR)
-    for t, (row0, nr, g) in enumerate(tiles):
-        tile_tab[t] = (row0, nr, g, sz_base)
-        rows = perm[row0: row0 + nr].astype(np.int64)
-        for i in range(I):
-            cnt = min(TPR, C - i * TPR)
-            r = np.arange(nr)[:, None]
-            kl = np.arange(cnt)[None, :]
-            c = (i * TPR + kl) + 0 * r                      # [nr, cnt] chunk index
-            s_rel = i * nr * TPR + r * cnt + kl             # tile-relative slot
-            slot = (row0 * C + s_rel).reshape(-1)
-            n_of = (rows[:, None] + 0 * kl).reshape(-1)
-            c_f = c.reshape(-1)
-            e = 32 * c_f[:, None] + np.arange(32)[None, :]
-            vals_blob[slot] = _encode_codes(q[n_of[:, None], e])
-            offs_blob[slot] = _encode_offs(o[n_of[:, None], e])
-            # scale/zero entries of the groups this chunk touches
-            per = max(1, cpc // g)
-            for j in range(per):
-                grp = gptr[n_of] + (c_f * cpc) // g + j
-                dst = sz_base + (s_rel.reshape(-1) * cpc) // g + j
-                if np.any(sz_filled[dst] & (sz_blob[dst] != sz_all[grp])):
-                    raise AssertionError("shared scale/zero entry disagrees")
-                sz_blob[dst] = sz_all[grp]
-                sz_filled[dst] = True
-        sz_base += nr * C * cpc // g
-    assert sz_base == n_groups and np.all(sz_filled)
-    off = section_offsets(N, K, nk, len(tiles), n_groups)
+    assert sz.size == n_groups
+    perm_pad = np.full(16 * T, -1, dtype=np.int32)
+    perm_pad[:N] = perm
+    off = section_offsets(N, K, nk, n_groups)
     blob = np.zeros(off["blob_bytes"], dtype=np.uint8)
-    blob[off["tiles"]: off["tiles"] + 16 * len(tiles)] = tile_tab.astype("<i4").view(np.uint8).reshape(-1)
-    blob[off["perm"]: off["perm"] + 4 * N] = perm.astype("<i4").view(np.uint8)
-    blob[off["vals"]: off["vals"] + 16 * N * C] = vals_blob.reshape(-1)
-    blob[off["offs"]: off["offs"] + 8 * N * C] = offs_blob.reshape(-1)
-    blob[off["sz"]: off["sz"] + 4 * n_groups] = sz_blob.astype("<u4").view(np.uint8)
-    return {"blob": blob, "offsets": off, "tiles": tile_tab, "perm": perm,
-            "vals": vals_blob, "offs": offs_blob, "sz": sz_blob}
+
+    def put(at, arr):
+        raw = np.ascontiguousarray(arr).astype("<u4").view(np.uint8).reshape(-1)
+        blob[at: at + raw.size] = raw
+
+    put(off["codes"], codes)
+    put(off["offs"], offs)
+    put(off["perm"], perm_pad.view(np.uint32))
+    put(off["sz"], sz)
+    return {"blob": blob, "offsets": off, "perm": perm_pad, "codes": codes, "offs": offs, "sz": sz}
 
 
-def decode(blob: np.ndarray, N: int, K: int, nk: int, RT: int, TPR: int):
-    """Inverse of build: blob -> per-element codes [N, kpr], offsets [N, kpr],
-    and per-row (scale, zero) lists, read through the same rules."""
-    C = K * nk // 128
-    cpc = cols_per_chunk(nk)
+def decode(blob: np.ndarray, N: int, K: int, nk: int, group_size):
+    """Inverse of build: blob -> per-element codes [N, K*nk/4] and offsets
+    [N, K*nk/4] in original row order, per-row scale|zero word lists and the
+    sorted-row permutation, read back through the same rules."""
+    gs = np.asarray(group_size, dtype=np.int64)
+    T, C, kpp = -(-N // 16), K // 256, 16 * nk
+    n_groups = int(np.sum(K // gs))
+    off = section_offsets(N, K, nk, n_groups)
+    u32 = lambda at, n: np.frombuffer(blob[at: at + 4 * n].tobytes(), dtype="<u4")
+    perm = np.frombuffer(blob[off["perm"]: off["perm"] + 64 * T].tobytes(), dtype="<i4")
+    cw = u32(off["codes"], T * C * 64 * 2 * nk).reshape(T, C, 64, 2 * nk)
+    ow = u32(off["offs"], T * C * 64 * nk).reshape(T, C, 64, nk)
+    szw = u32(off["sz"], n_groups)
     kpr = K * nk // 4
-    # the tile table's size is implied by the group sizes, which the tile
-    # table itself records; read tiles until the rows are covered
-    tiles, rows_seen, t = [], 0, 0
-    while rows_seen < N:
-        row0, nr, g, szb = np.frombuffer(blob[16 * t: 16 * t + 16].tobytes(), dtype="<i4")
-        tiles.append((int(row0), int(nr), int(g), int(szb)))
-        rows_seen += int(nr)
-        t += 1
-    n_groups = sum(nr * K // g for (_, nr, g, _) in tiles)
-    off = section_offsets(N, K, nk, len(tiles), n_groups)
-    perm = np.frombuffer(blob[off["perm"]: off["perm"] + 4 * N].tobytes(), dtype="<i4")
-    vb = blob[off["vals"]: off["vals"] + 16 * N * C].reshape(N * C, 4, 4)
-    ob = blob[off["offs"]: off["offs"] + 8 * N * C].reshape(N * C, 2, 4)
-    vd = vb.astype(np.uint32)
-    vd = vd[..., 0] | (vd[..., 1] << 8) | (vd[..., 2] << 16) | (vd[..., 3] << 24)   # [S, 4]
-    od = ob.astype(np.uint32)
-    od = od[..., 0] | (od[..., 1] << 8) | (od[..., 2] << 16) | (od[..., 3] << 24)   # [S, 2]
-    szb = np.frombuffer(blob[off["sz"]: off["sz"] + 4 * n_groups].tobytes(), dtype="<u4")
     q = np.zeros((N, kpr), dtype=np.uint8)
     o = np.zeros((N, kpr), dtype=np.uint8)
     sz_rows = {}
-    I = -(-C // TPR)
-    for (row0, nr, g, sz_base) in tiles:
-        for r in range(nr):
-            n = int(perm[row0 + r])
-            ng = K // g
-            sz_rows[n] = np.zeros(ng, dtype=np.uint32)
-            for c in range(C):
-                i, kl = divmod(c, TPR)
-                cnt = min(TPR, C - i * TPR)
-                s_rel = i * nr * TPR + r * cnt + kl
-                slot = row0 * C + s_rel
-                for e in range(32):
-                    d, m = divmod(e, 8)
-                    k = m // 2 if m % 2 == 0 else 4 + m // 2
-                    q[n, 32 * c + e] = (vd[slot, d] >> (4 * k)) & 0xF
-                    D, rest = divmod(e, 16)
-                    qq, b = divmod(rest, 4)
-                    o[n, 32 * c + e] = (od[slot, D] >> (8 * b + 2 * qq)) & 3
-                for j in range(max(1, cpc // g)):
-                    sz_rows[n][(c * cpc) // g + j] = szb[sz_base + (s_rel * cpc) // g + j]
-    return q, o, sz_rows, perm
+    at = 0
+    for b in range(T):
+        for c in range(C):
+            for r in range(16):
+                i = 16 * b + r
+                if i >= N:
+                    break
+                n = int(perm[i])
+                for qq in range(4):
+                    lane = r + 16 * qq
+                    e0 = kpp * (4 * c + qq)
+                    for m in range(kpp):
+                        dw, k = divmod(m, 8)
+                        q[n, e0 + m] = (cw[b, c, lane, dw] >> (4 * NIB[nk][k])) & 0xF
+                        if nk == 2:
+                            word, bit = divmod(m, 16)
+                            o[n, e0 + m] = (ow[b, c, lane, word] >> (2 * bit)) & 3
+                        else:
+                            o[n, e0 + m] = (ow[b, c, lane, 0] >> off14_bit(m)) & 3
+                per = 256 // int(gs[n])
+                sz_rows.setdefault(n, np.zeros(K // int(gs[n]), dtype=np.uint32))
+                sz_rows[n][c * per: (c + 1) * per] = szw[at: at + per]
+                at += per
+    assert at == n_groups
+    return q, o, sz_rows, perm[:N]

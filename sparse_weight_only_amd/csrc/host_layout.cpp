@@ -1,24 +1,30 @@
 // Layer descriptor and kernel layout of the 2bit-CSR arrays.
 //
-// The kernel layout is a permutation of the canonical bits (no padding and
-// no duplication) so that the SparseGemv kernel reads codes with 16-byte,
-// offsets with 8-byte and scale|zero words with 4..16-byte coalesced loads:
-//  - rows sorted by group size (ascending), ascending row index within a size;
-//  - tiles of up to rt sorted rows of one group size, one workgroup each;
-//  - a chunk = 32 consecutive kept elements of a row (cpc = 128/nk columns);
-//    chunk c of a row goes to k-lane c % tpr at iteration c / tpr, and its
-//    slot is row0*C + i*nr*tpr + r*cnt_i + kl (cnt_i chunks per row in
-//    iteration i: tpr, or the remainder in the last one);
-//  - inside a chunk, codes dword d holds elements 8d..8d+7 with nibble k
-//    holding element 8d + 2k (k < 4) or 8d + 2(k-4) + 1 (k >= 4); offsets
-//    dword D holds elements 16D..16D+15, element 16D + 4q + b at bits 8b + 2q;
-//  - scale|zero<<16 words: chunk at tile slot s uses sz_base + (s*cpc)/g + j,
-//    j < max(1, cpc/g), so chunks sharing a group share one stored word.
+// The kernel layout is a permutation of the canonical bits, with zero
+// padding only for the rows of a last, partial row block, arranged for the
+// matrix-core kernel (v_smfmac_f32_16x16x64_f16: 16 rows x 64 dense columns
+// per instruction, A operand 2-of-4 sparse with 2-bit indices):
+//  - sorted rows: rows ordered by group size (ascending, stable);
+//  - row block b: sorted rows 16b .. 16b+15 (T = ceil(N/16) blocks);
+//  - piece (i, c, q): sorted row i, dense columns 256c + 64q .. 256c + 64q + 63,
+//    i.e. its 16*nk consecutive kept elements starting at 16*nk*(4c + q);
+//  - record (b, c) of the code and offset sections: 64 lanes, lane r + 16q
+//    holding piece (16b + r, c, q);
+//  - codes of a piece: little-endian dwords of 8 consecutive elements; element
+//    k of a dword sits at nibble [0,4,1,5,2,6,3,7][k] (2:4) or
+//    [0,1,4,5,2,3,6,7][k] (1:4);
+//  - offsets of a piece: 2:4 = the canonical 2-bit fields (element m at bits
+//    2m of a little-endian 64-bit word); 1:4 = one dword, element m at bit
+//    16*((m/4)%2) + (m/4 < 2 ? [0,4,10,14] : [2,6,8,12])[m%4];
+//  - perm: original row of each sorted row, -1 for padding rows;
+//  - scale|zero<<16 words: records (b, c) in order, each the rows of block b
+//    in order, each with its 256/g words of chunk c (groups c*256/g ..).
 // Reference: the first contribution item of the page "Efficient LLM ad
 // generation via model compression and parallel verification" (translation
 // of arXiv 2605.11582), which introduces the index-compressed 2bit-CSR format
 // but leaves its bit layout open.
 #include <algorithm>
+#include <cmath>
 #include <numeric>
 #include <vector>
 
@@ -28,69 +34,54 @@ using namespace sgemv;
 
 namespace {
 
-struct Tile { int32_t row0, nr, g; };
-
-// Sorted row order (by group size, stable) and the tile list.
-void order_and_tiles(const int32_t* gs, int32_t N, int32_t rt, std::vector<int32_t>& perm,
-                     std::vector<Tile>& tiles) {
-  perm.resize(N);
+std::vector<int32_t> sorted_rows(const int32_t* gs, int32_t N) {
+  std::vector<int32_t> perm(N);
   std::iota(perm.begin(), perm.end(), 0);
   std::stable_sort(perm.begin(), perm.end(), [&](int32_t a, int32_t b) { return gs[a] < gs[b]; });
-  tiles.clear();
-  int32_t i = 0;
-  while (i < N) {
-    int32_t g = gs[perm[i]], j = i;
-    while (j < N && gs[perm[j]] == g) ++j;
-    for (int32_t r0 = i; r0 < j; r0 += rt) tiles.push_back({r0, std::min(rt, j - r0), g});
-    i = j;
-  }
+  return perm;
 }
+
+constexpr int kNib24[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+constexpr int kNib14[8] = {0, 1, 4, 5, 2, 3, 6, 7};
+constexpr int kOff14Real[4] = {0, 4, 10, 14};
+constexpr int kOff14Dummy[4] = {2, 6, 8, 12};
 
 }  // namespace
 
 extern "C" int sgemv_describe(int32_t N, int32_t K, int32_t nk, const int32_t* group_size,
-                              int32_t rt, int32_t tpr, sgemv_desc* out) {
+                              sgemv_desc* out) {
   if (!group_size || !out) return SGEMV_EINVAL;
-  if (N < 1 || K < 256 || K % 256 != 0 || (nk != 1 && nk != 2)) return SGEMV_EINVAL;
-  if ((int64_t)N * K * nk / 4 >= ((int64_t)1 << 31)) return SGEMV_ESIZE;
+  if (N < 1 || K < kChunkCols || K % kChunkCols != 0 || (nk != 1 && nk != 2)) return SGEMV_EINVAL;
+  if (K / kChunkCols > kMaxChunks) return SGEMV_ESIZE;
   int g_min = 1 << 30, g_max = 0;
   int64_t n_groups = 0;
+  sgemv_desc d;
+  memset(&d, 0, sizeof d);
   for (int32_t n = 0; n < N; ++n) {
-    int g = group_size[n];
+    const int g = group_size[n];
     if (!valid_group(g, K)) return SGEMV_EINVAL;
     g_min = std::min(g_min, g);
     g_max = std::max(g_max, g);
     n_groups += K / g;
+    d.class_rows[ilog2(g / 32)] += 1;
   }
-  const int cpc = cols_per_chunk(nk);
-  const int32_t C = K * nk / 128;
-  if (rt == 0 && tpr == 0) {
-    // default: 256-lane workgroups, 32 lanes per row (two rows per wave), or
-    // 64 when a row has more than 128 chunks (at most 4 chunks per lane)
-    tpr = C > 128 ? 64 : 32;
-    while (tpr > 4 && tpr / 2 >= C) tpr /= 2;
-    rt = 256 / tpr;
-  }
-  if (!layout_params_ok(K, C, cpc, tpr, rt, g_max)) return SGEMV_ESIZE;
-  std::vector<int32_t> perm;
-  std::vector<Tile> tiles;
-  order_and_tiles(group_size, N, rt, perm, tiles);
-  sgemv_desc d;
-  memset(&d, 0, sizeof d);
-  d.N = N; d.K = K; d.nk = nk; d.rt = rt; d.tpr = tpr;
-  d.n_tiles = (int32_t)tiles.size();
+  const int32_t T = (N + kBlockRows - 1) / kBlockRows, C = K / kChunkCols;
+  d.N = N; d.K = K; d.nk = nk;
+  d.n_blocks = T;
+  d.chunks = C;
   d.g_min = g_min; d.g_max = g_max;
-  for (int32_t n = 0; n < N; ++n) d.class_rows[ilog2(group_size[n] / 32)] += 1;
   d.kept = (int64_t)N * K * nk / 4;
   d.vals_bytes = d.kept / 2;
   d.offs_bytes = d.kept / 4;
   d.n_groups = n_groups;
-  d.off_tiles = 0;
-  d.off_perm = align_up(16 * (int64_t)d.n_tiles);
-  d.off_vals = align_up(d.off_perm + 4 * (int64_t)N);
-  d.off_offs = align_up(d.off_vals + 16 * (int64_t)N * C);
-  d.off_sz = align_up(d.off_offs + 8 * (int64_t)N * C);
-  d.blob_bytes = align_up(d.off_sz + 4 * n_groups);
+  const int64_t records = (int64_t)T * C * 64;
+  d.off_codes = 0;
+  d.off_offs = align_up(records * piece_code_bytes(nk));
+  d.off_perm = align_up(d.off_offs + records * piece_offs_bytes(nk));
+  d.off_sz = align_up(d.off_perm + 4 * (int64_t)T * kBlockRows);
+  // 8 spare bytes after the words: a lane reads two words where it needs one
+  d.blob_bytes = align_up(d.off_sz + 4 * n_groups + 8);
+  if (d.blob_bytes >= ((int64_t)1 << 31)) return SGEMV_ESIZE;
   *out = d;
   return SGEMV_OK;
 }
@@ -100,81 +91,92 @@ extern "C" int sgemv_layout(const sgemv_desc* d, const uint8_t* vals, const uint
                             void* blob_v) {
   if (!d || !vals || !offs || !scale || !zero || !gptr || !blob_v) return SGEMV_EINVAL;
   const int32_t N = d->N, K = d->K, nk = d->nk;
-  if (N < 1 || K < 256 || K % 256 || (nk != 1 && nk != 2)) return SGEMV_EINVAL;
+  if (N < 1 || K < kChunkCols || K % kChunkCols || (nk != 1 && nk != 2)) return SGEMV_EINVAL;
   // group sizes from the ragged row pointer of the scale/zero arrays
   std::vector<int32_t> gs(N);
   if (gptr[0] != 0) return SGEMV_EINVAL;
   for (int32_t n = 0; n < N; ++n) {
-    int32_t ng = gptr[n + 1] - gptr[n];
+    const int32_t ng = gptr[n + 1] - gptr[n];
     if (ng <= 0 || K % ng) return SGEMV_EINVAL;
     gs[n] = K / ng;
     if (!valid_group(gs[n], K)) return SGEMV_EINVAL;
   }
   sgemv_desc chk;
-  int rc = sgemv_describe(N, K, nk, gs.data(), d->rt, d->tpr, &chk);
+  const int rc = sgemv_describe(N, K, nk, gs.data(), &chk);
   if (rc) return rc;
   if (memcmp(&chk, d, sizeof chk) != 0) return SGEMV_ESIZE;
-  const int cpc = cols_per_chunk(nk);
-  const int32_t C = K * nk / 128, tpr = d->tpr, kpr = K * nk / 4;
-  const int32_t I = (C + tpr - 1) / tpr;
-  std::vector<int32_t> perm;
-  std::vector<Tile> tiles;
-  order_and_tiles(gs.data(), N, d->rt, perm, tiles);
+  const int32_t T = d->n_blocks, C = d->chunks, kpr = K * nk / 4;
+  const int pcb = piece_code_bytes(nk), pob = piece_offs_bytes(nk), kpp = 16 * nk;
+  const std::vector<int32_t> perm = sorted_rows(gs.data(), N);
+  // The kernel holds each weight as the FP16 value (code - zero) * scale:
+  // reject layers where that rounds outside the FP16 range.
+  for (int32_t n = 0; n < N; ++n) {
+    const uint8_t* vrow = vals + (int64_t)n * (kpr / 2);
+    const int32_t kpg = gs[n] * nk / 4;                // kept elements per group
+    for (int32_t g = 0; g < kpr / kpg; ++g) {
+      int lo = 15, hi = 0;
+      for (int32_t j = g * kpg; j < (g + 1) * kpg; ++j) {
+        const int code = (vrow[j >> 1] >> (4 * (j & 1))) & 0xF;
+        lo = std::min(lo, code);
+        hi = std::max(hi, code);
+      }
+      const int64_t grp = gptr[n] + g;
+      const double s = f16_to_f64(scale[grp]), z = f16_to_f64(zero[grp]);
+      if (!f16_finite(f64_to_f16((lo - z) * s)) || !f16_finite(f64_to_f16((hi - z) * s))) return SGEMV_EINVAL;
+    }
+  }
   uint8_t* blob = (uint8_t*)blob_v;
   memset(blob, 0, (size_t)d->blob_bytes);
-  int32_t* tab = (int32_t*)(blob + d->off_tiles);
+  uint8_t* cb = blob + d->off_codes;
+  uint8_t* ob = blob + d->off_offs;
   int32_t* pm = (int32_t*)(blob + d->off_perm);
-  uint32_t* vb = (uint32_t*)(blob + d->off_vals);
-  uint32_t* ob = (uint32_t*)(blob + d->off_offs);
   uint32_t* szb = (uint32_t*)(blob + d->off_sz);
-  for (int32_t i = 0; i < N; ++i) pm[i] = perm[i];
-  int64_t sz_base = 0;
-  for (size_t t = 0; t < tiles.size(); ++t) {
-    const Tile& T = tiles[t];
-    tab[4 * t + 0] = T.row0;
-    tab[4 * t + 1] = T.nr;
-    tab[4 * t + 2] = T.g;
-    tab[4 * t + 3] = (int32_t)sz_base;
-    for (int32_t r = 0; r < T.nr; ++r) {
-      const int32_t n = perm[T.row0 + r];
-      const uint8_t* vrow = vals + (int64_t)n * (kpr / 2);
-      const uint8_t* orow = offs + (int64_t)n * (kpr / 4);
-      for (int32_t c = 0; c < C; ++c) {
-        const int32_t i = c / tpr, kl = c % tpr;
-        const int32_t cnt = (i == I - 1) ? C - (I - 1) * tpr : tpr;
-        const int64_t s_rel = (int64_t)i * T.nr * tpr + (int64_t)r * cnt + kl;
-        const int64_t slot = (int64_t)T.row0 * C + s_rel;
-        const int64_t e0 = (int64_t)c * kChunkElems;
-        for (int dw = 0; dw < 4; ++dw) {
-          uint32_t word = 0;
-          for (int k = 0; k < 8; ++k) {
-            int m = (k < 4) ? 2 * k : 2 * (k - 4) + 1;
-            int64_t j = e0 + 8 * dw + m;
-            uint32_t code = (vrow[j >> 1] >> (4 * (j & 1))) & 0xFu;
-            word |= code << (4 * k);
-          }
-          vb[4 * slot + dw] = word;
-        }
-        for (int D = 0; D < 2; ++D) {
-          uint32_t word = 0;
-          for (int q = 0; q < 4; ++q)
-            for (int b = 0; b < 4; ++b) {
-              int64_t j = e0 + 16 * D + 4 * q + b;
-              uint32_t o = (orow[j >> 2] >> (2 * (j & 3))) & 3u;
-              word |= o << (8 * b + 2 * q);
+  for (int32_t i = 0; i < T * kBlockRows; ++i) pm[i] = i < N ? perm[i] : -1;
+  int64_t szw = 0;
+  for (int32_t b = 0; b < T; ++b) {
+    for (int32_t c = 0; c < C; ++c) {
+      for (int32_t r = 0; r < kBlockRows; ++r) {
+        const int32_t i = b * kBlockRows + r;
+        if (i >= N) break;
+        const int32_t n = perm[i];
+        const uint8_t* vrow = vals + (int64_t)n * (kpr / 2);
+        const uint8_t* orow = offs + (int64_t)n * (kpr / 4);
+        for (int q = 0; q < 4; ++q) {
+          const int64_t rec = ((int64_t)b * C + c) * 64 + r + 16 * q;
+          const int64_t e0 = (int64_t)kpp * (4 * c + q);        // first kept element of the piece
+          // codes: dwords of 8 elements with the nibble order of the N:M choice
+          for (int dw = 0; dw < pcb / 4; ++dw) {
+            uint32_t word = 0;
+            for (int k = 0; k < 8; ++k) {
+              const int64_t j = e0 + 8 * dw + k;
+              const uint32_t code = (vrow[j >> 1] >> (4 * (j & 1))) & 0xFu;
+              word |= code << (4 * (nk == 2 ? kNib24[k] : kNib14[k]));
             }
-          ob[2 * slot + D] = word;
+            memcpy(cb + rec * pcb + 4 * dw, &word, 4);
+          }
+          // offsets
+          if (nk == 2) {
+            memcpy(ob + rec * pob, orow + e0 / 4, pob);        // canonical bytes, unchanged
+          } else {
+            uint32_t word = 0;
+            for (int m = 0; m < 16; ++m) {
+              const int64_t j = e0 + m;
+              const uint32_t o = (orow[j >> 2] >> (2 * (j & 3))) & 3u;
+              const int t = m / 4, e = m % 4;
+              word |= o << (16 * (t % 2) + (t < 2 ? kOff14Real[e] : kOff14Dummy[e]));
+            }
+            memcpy(ob + rec * pob, &word, 4);
+          }
         }
-        const int per = std::max(1, cpc / T.g);
+        // scale|zero words of chunk c of this row
+        const int per = kChunkCols / gs[n];
         for (int j = 0; j < per; ++j) {
-          int64_t src = gptr[n] + ((int64_t)c * cpc) / T.g + j;
-          int64_t dst = sz_base + (s_rel * cpc) / T.g + j;
-          szb[dst] = (uint32_t)scale[src] | ((uint32_t)zero[src] << 16);
+          const int64_t src = gptr[n] + (int64_t)c * per + j;
+          szb[szw++] = (uint32_t)scale[src] | ((uint32_t)zero[src] << 16);
         }
       }
     }
-    sz_base += (int64_t)T.nr * C * cpc / T.g;
   }
-  if (sz_base != d->n_groups) return SGEMV_ESIZE;
+  if (szw != d->n_groups) return SGEMV_ESIZE;
   return SGEMV_OK;
 }

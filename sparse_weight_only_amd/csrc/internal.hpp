@@ -8,11 +8,8 @@
 
 namespace sgemv {
 
-constexpr int kChunkElems = 32;            // kept elements per chunk (16 B codes, 8 B offsets)
-constexpr int kMaxChunksPerThread = 8;     // register budget of the kernels
 constexpr int64_t kAlign = 256;            // blob section alignment
 
-inline int cols_per_chunk(int nk) { return 128 / nk; }          // 64 at 2:4, 128 at 1:4
 inline int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline bool valid_group(int g, int K) { return (g == 32 || g == 64 || g == 128 || g == 256) && K % g == 0; }
 inline int ilog2(int v) { int l = 0; while ((1 << l) < v) ++l; return l; }
@@ -59,38 +56,44 @@ inline double f16_to_f64(uint16_t h) {
 
 inline bool f16_finite(uint16_t h) { return ((h >> 10) & 31) != 31; }
 
-// Kernel geometry of a layout: a tile of rt rows with tpr lanes per row is
-// one workgroup of min(256, rt*tpr) lanes, each lane owning rpl rows.
-struct Geometry { int wg, rpl, iters, imax, xmax; };
-inline int bucket(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
-inline Geometry geometry(int32_t K, int32_t C, int32_t tpr, int32_t rt) {
-  Geometry g;
-  const int32_t slots = rt * tpr;
-  g.wg = slots < 256 ? slots : 256;
-  g.rpl = slots / g.wg;
-  g.iters = (C + tpr - 1) / tpr;
-  g.imax = bucket(g.iters);
-  g.xmax = ((K / 8 + g.wg - 1) / g.wg) <= 2 ? 2 : 8;
-  return g;
-}
+// Dense columns per column chunk; a chunk of one row is split into 4 pieces
+// of 64 columns, one per lane block of the matrix-core instruction.
+constexpr int kChunkCols = 256;
+constexpr int kBlockRows = 16;             // rows per row block (matrix-core tile height)
+constexpr int kMaxChunks = 128;            // K <= 32768
+constexpr int kMaxWaves = 16;              // waves per workgroup
+constexpr int kMaxChunksPerWave = 8;       // register budget of the kernel
 
-// Layout parameters the kernels accept: tpr lanes per row (a power of two in
-// [4, 64], so a row's lanes sit in one wave); rt*tpr a power of two in
-// [64, 1024] giving 1, 2 or 4 rows per lane; at most 8 chunks per row-lane and
-// 8 chunks per lane in all; at most 8 x blocks of 8 columns staged per lane;
-// chunks that share a scale word owned by the same iteration.
-inline bool layout_params_ok(int32_t K, int32_t C, int cpc, int32_t tpr, int32_t rt, int g_max) {
-  if (tpr < 4 || tpr > 64 || (tpr & (tpr - 1))) return false;
-  const int32_t slots = rt * tpr;
-  if (rt < 1 || slots < 64 || slots > 1024 || (slots & (slots - 1))) return false;
-  const Geometry g = geometry(K, C, tpr, rt);
-  if (g.iters > kMaxChunksPerThread || g.rpl * g.imax > kMaxChunksPerThread) return false;
-  if ((K / 8 + g.wg - 1) / g.wg > 8) return false;
-  if (g_max > cpc) {
-    const int share = g_max / cpc;   // chunks sharing one scale/zero word
-    if (tpr % share || C % share) return false;
-  }
-  return true;
+inline int bucket(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
+
+// Bytes of one piece (one row, 64 dense columns) in the code and offset sections.
+inline int piece_code_bytes(int nk) { return 8 * nk; }    // 16 kept (1:4) or 32 kept (2:4) nibbles
+inline int piece_offs_bytes(int nk) { return 4 * nk; }    // 2 bits per kept element
+
+// Launch geometry for (chunks per row, row blocks, batch): how the column
+// chunks of a row block are split over the waves of its workgroup and how
+// many chunks of x are staged in LDS at once.
+struct Launch { int waves, cpw, imax, phase, xloads, xmax; int64_t lds; };
+inline Launch launch_geometry(int C, int T, int B) {
+  Launch L;
+  int cpw = 4;
+  // smaller slices when the layer has few row blocks, so the grid has
+  // enough waves to cover the chip (256 CUs x 4 SIMDs, two waves each)
+  while (cpw > 1 && (int64_t)T * ((C + cpw - 1) / cpw) < 2048) cpw /= 2;
+  if ((C + cpw - 1) / cpw > kMaxWaves) cpw = (C + kMaxWaves - 1) / kMaxWaves;
+  L.cpw = cpw;
+  L.waves = (C + cpw - 1) / cpw;
+  L.imax = bucket(cpw);
+  // x of phase chunks staged at once: B * phase <= 16 keeps the staging at
+  // most 8 16-byte loads per lane
+  int ph = 1;
+  while (ph * 2 <= cpw && B * ph * 2 <= 16) ph *= 2;
+  if (ph < cpw && B * cpw <= 16) ph = cpw;
+  L.phase = ph;
+  L.xloads = (B * ph * 32 + 63) / 64;
+  L.xmax = bucket(L.xloads);
+  L.lds = (int64_t)L.waves * B * ph * 512 + (int64_t)B * kBlockRows * kMaxWaves * 4;
+  return L;
 }
 
 }  // namespace sgemv

@@ -1,4 +1,4 @@
-// Device code of the SparseGemv kernels for gfx950 (MI355X, CDNA4, wave64).
+// Device code of the SparseGemv kernel for gfx950 (MI355X, CDNA4, wave64).
 //
 // y = W' x for an N:M-sparse (2:4 or 1:4 along K) INT4 weight matrix with
 // per-group FP16 scale and zero, FP16 activations and FP32 accumulation: the
@@ -8,325 +8,60 @@
 // kernel". That section stops before describing its kernel; the design here
 // is our own for CDNA4.
 //
-// One workgroup per tile of rt rows of one group size; tpr lanes per row
-// split the row's 32-element chunks round-robin (chunk c -> lane c % tpr,
-// iteration c / tpr), so that a row's lanes are consecutive in one wave.
-//  1. every lane issues all of its weight loads first: a 16-byte code load,
-//     an 8-byte offset load and a 4/8/16-byte scale|zero load per chunk,
-//     coalesced across the workgroup by the kernel layout;
-//  2. the workgroup stages x into LDS as byte planes (per 8 columns: 8 low
-//     bytes, then 8 high bytes), one 16-byte pad after every chunk's columns
-//     so that neighbouring lanes start in different banks;
-//  3. per 4 kept elements: the 2-bit offsets become v_perm byte selectors
-//     that pick the matching x halves out of the planes; nibbles become FP16
-//     (q - z) exactly via the 0x6400 exponent trick; v_dot2_f32_f16
-//     accumulates in FP32; the FP16 scale multiplies each group's partial;
-//  4. a DPP reduction over the row's lanes; the row's last lane writes y in
-//     FP16 (round to nearest even) at the row's original position.
-// The products (q - z) * x are exact in FP32, so the only roundings are the
-// FP32 accumulation and the final FP16 conversion.
+// The 2-of-4 sparse matrix-core instruction v_smfmac_f32_16x16x64_f16 does
+// the selection of x and the dot product: its A operand is 16 rows x 64
+// dense columns given as 2 values per group of 4 columns plus their 2-bit
+// in-group indices, which is exactly the 2bit-CSR encoding of a 2:4 row.
+// Per lane (row r = lane % 16, column block q = lane / 16) and instruction:
+// 8 A values (4 groups of 4 columns), a 16-bit index field, and 16 x values
+// of the B operand (column b = lane % 16 is batch vector b).
+//
+// One workgroup per row block (16 rows sorted by group size); its W waves
+// split the row's K/256 column chunks, wave w taking chunks
+// [w*cpw, (w+1)*cpw). Per wave:
+//  1. loads, all issued up front and in this order: the wave's x slice
+//     (16-byte loads, cached), then codes, offsets and scale|zero words of
+//     every chunk (non-temporal: the weights are read once); lanes without
+//     work read out of range and get zeros without touching memory;
+//  2. the x slice goes to this wave's own LDS region (no barrier with other
+//     waves: a wave waits only for its own loads);
+//  3. per 64-column step: codes -> FP16 (q - z) exactly (0x6400 exponent
+//     trick), times the FP16 scale -> the A operand; 1:4 rows put each kept
+//     value in one slot of its group and 0 in the other; the offsets are the
+//     index field as stored; two ds_read_b128 give the B operand; one
+//     v_smfmac accumulates 16 rows x 16 columns in FP32;
+//  4. the waves' partial sums meet in LDS; 16*B lanes add them in wave order
+//     and write y in FP16 (round to nearest even) at the rows' original
+//     positions.
+// Large batches stage x in phases of `phase` chunks, prefetching the next
+// phase's slice while the current one is computed.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace sgemv_dev {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __fp16 hp16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h16 __attribute__((ext_vector_type(16)));
+typedef float f4 __attribute__((ext_vector_type(4)));
 
 struct KParams {
-  const int32_t* tiles;  // [n_tiles][4] = row0, nr, g, sz_base
-  const int32_t* perm;   // [N] original row of each sorted row
-  const u32x4* vals;     // [slots] 16-byte code chunks
-  const u32x2* offs;     // [slots] 8-byte offset chunks
-  const uint32_t* sz;    // [n_groups] scale | zero << 16
-  const u32x4* x;        // [B][K/8]
-  uint16_t* y;           // [B][N]
-  int32_t N, K, C, B;
-  int32_t tpr_log2;
-  int32_t phase_iters;   // chunk iterations whose x columns are staged at once
-  int32_t pass_log2;     // workgroups per tile = 1 << pass_log2 (batched kernels)
-  int32_t rt;            // rows per tile
-  int32_t cls_tile[5];   // first tile of each group-size class (32, 64, 128, 256), then n_tiles
-  int32_t cls_row[5];    // first sorted row of each class, then N
-  int32_t cls_sz[4];     // first scale|zero word of each class
+  const uint8_t* blob;   // kernel-layout blob
+  const uint16_t* x;     // [B][K] FP16
+  uint16_t* y;           // [B][N] FP16
+  uint32_t blob_bytes;
+  uint32_t off_codes, off_offs, off_perm, off_sz;
+  int32_t N, K, B, C;    // C = K / 256 column chunks
+  int32_t cpw;           // column chunks per wave
+  int32_t phase;         // chunks whose x slice is staged at once
+  int32_t T;             // row blocks (= workgroups)
+  int32_t cls_row[5];    // first sorted row of group size 32, 64, 128, 256, then N
 };
-
-// Tile geometry from the class table (no dependent load of the blob's tile table).
-struct TileGeo { int row0, nr, g, sz_base; };
-__device__ __forceinline__ TileGeo tile_geo(const KParams& p, int tile) {
-  // class c = last class whose first tile is <= tile; the flags are monotone,
-  // so telescoping sums pick the class's values without an indexed lookup
-  const int f1 = tile >= p.cls_tile[1], f2 = tile >= p.cls_tile[2], f3 = tile >= p.cls_tile[3];
-  const int c = f1 + f2 + f3;
-  auto pick = [&](const int32_t* a) {
-    return a[0] + f1 * (a[1] - a[0]) + f2 * (a[2] - a[1]) + f3 * (a[3] - a[2]);
-  };
-  const int ct = pick(p.cls_tile), cr = pick(p.cls_row), cz = pick(p.cls_sz), end = pick(p.cls_row + 1);
-  TileGeo t;
-  t.g = 32 << c;
-  t.row0 = cr + (tile - ct) * p.rt;
-  t.nr = end - t.row0 < p.rt ? end - t.row0 : p.rt;
-  t.sz_base = cz + (t.row0 - cr) * (p.K >> (5 + c));
-  return t;
-}
-
-__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
-// (a & m) | c in one v_and_or_b32 (m in an SGPR, c in a VGPR: one constant-bus read).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
-  return r;
-}
-
-__device__ __forceinline__ f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
-
-__device__ __forceinline__ float dot2(f16x2 a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(hp16x2, a), __builtin_bit_cast(hp16x2, b), c, false);
-}
-
-// Constants kept in VGPRs so that v_and_or_b32 can take them.
-struct Consts {
-  uint32_t magic;     // 0x64006400: two FP16 1024.0
-  uint32_t sel_or;    // +4 added to the selector bytes of the second group (2:4) or odd elements (1:4)
-};
-
-// FP16 (q - z) pairs of one code dword: (e0,e1), (e2,e3), (e4,e5), (e6,e7).
-// 0x6400 | n is the FP16 value 1024 + n; 0x6400 | (n << 4) is 1024 + 16 n.
-struct Deq { f16x2 w01, w23, w45, w67; };
-__device__ __forceinline__ Deq dequant_dword(uint32_t v, f16x2 zc1, f16x2 zc2, const Consts& k) {
-  const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  Deq d;
-  const uint32_t v8 = v >> 8;
-  d.w01 = as_f16x2(and_or(v, 0x000F000Fu, k.magic)) + zc1;                                  // n - z
-  d.w23 = __builtin_elementwise_fma(as_f16x2(and_or(v, 0x00F000F0u, k.magic)), sixteenth, zc2);  // (1024+16n)/16 - 64 - z
-  d.w45 = as_f16x2(and_or(v8, 0x000F000Fu, k.magic)) + zc1;
-  d.w67 = __builtin_elementwise_fma(as_f16x2(and_or(v8, 0x00F000F0u, k.magic)), sixteenth, zc2);
-  return d;
-}
-
-__device__ __forceinline__ void zero_consts(uint32_t szw, f16x2& zc1, f16x2& zc2, float& sf) {
-  const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)(szw >> 16));
-  const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
-  const _Float16 a = (_Float16)-1024.0f - z;  // exact: integers up to 1039
-  const _Float16 b = (_Float16)-64.0f - z;
-  zc1 = f16x2{a, a};
-  zc2 = f16x2{b, b};
-  sf = (float)s;
-}
-
-// Byte selectors of quad qq (4 consecutive kept elements of the chunk):
-// offsets of its elements in the four bytes, +4 where the element's x lives
-// in the second 4-column half of the 8-column plane block.
-__device__ __forceinline__ uint32_t quad_selector(const u32x2 o, int qq, const Consts& k) {
-  const uint32_t w = (qq < 4) ? o.x : o.y;
-  const int sh = 2 * (qq & 3);
-  return and_or(sh ? (w >> sh) : w, 0x03030303u, k.sel_or);
-}
-
-// x halves of the kept elements of one 2:4 quad (groups 2qq, 2qq+1 of the
-// chunk, both inside the 8-column plane block X).
-__device__ __forceinline__ void xsel_2of4(const u32x4 X, uint32_t M, uint32_t& xab, uint32_t& xcd) {
-  const uint32_t lo = perm_b32(X.y, X.x, M);
-  const uint32_t hi = perm_b32(X.w, X.z, M);
-  xab = perm_b32(hi, lo, 0x05010400u);
-  xcd = perm_b32(hi, lo, 0x07030602u);
-}
-
-// x halves of one 1:4 quad (4 groups, 16 columns: plane blocks X and Y).
-__device__ __forceinline__ void xsel_1of4(const u32x4 X, const u32x4 Y, uint32_t M, uint32_t& xab, uint32_t& xcd) {
-  const uint32_t lo = perm_b32(X.y, X.x, M);
-  const uint32_t hi = perm_b32(X.w, X.z, M);
-  xab = perm_b32(hi, lo, 0x05010400u);
-  const uint32_t lo2 = perm_b32(Y.y, Y.x, M);
-  const uint32_t hi2 = perm_b32(Y.w, Y.z, M);
-  xcd = perm_b32(hi2, lo2, 0x07030602u);
-}
-
-// One chunk (32 kept elements) of one row against B activation vectors
-// (x planes of the chunk at xc, ldsb blocks apart per vector).
-template <int NK, int G, int BMAX, int SPC>
-__device__ __forceinline__ void chunk_compute(const u32x4 v, const u32x2 o, const uint32_t (&s)[SPC],
-                                              const u32x4* __restrict__ xc, int ldsb, int B,
-                                              float (&tot)[BMAX], const Consts& k) {
-  constexpr int CPC = 128 / NK;
-  constexpr int QPG = (G >= CPC) ? 8 : (8 * G) / CPC;  // quads (4 kept elements) per scale group
-#pragma unroll
-  for (int q0 = 0; q0 < 8; q0 += QPG) {
-    f16x2 zc1, zc2;
-    float sf;
-    zero_consts(s[(G >= CPC) ? 0 : q0 / QPG], zc1, zc2, sf);
-    float acc[BMAX];
-#pragma unroll
-    for (int b = 0; b < BMAX; ++b) acc[b] = 0.0f;
-#pragma unroll
-    for (int qq = q0; qq < q0 + QPG; qq += 2) {
-      const Deq d = dequant_dword(v[qq >> 1], zc1, zc2, k);
-      const uint32_t MA = quad_selector(o, qq, k);
-      const uint32_t MB = quad_selector(o, qq + 1, k);
-#pragma unroll
-      for (int b = 0; b < BMAX; ++b) {
-        if (BMAX == 1 || b < B) {
-          const u32x4* xb = xc + b * ldsb;
-          uint32_t xab, xcd, xef, xgh;
-          if constexpr (NK == 2) {
-            xsel_2of4(xb[qq], MA, xab, xcd);
-            xsel_2of4(xb[qq + 1], MB, xef, xgh);
-          } else {
-            xsel_1of4(xb[2 * qq], xb[2 * qq + 1], MA, xab, xcd);
-            xsel_1of4(xb[2 * qq + 2], xb[2 * qq + 3], MB, xef, xgh);
-          }
-          float a = acc[b];
-          a = dot2(d.w01, xab, a);
-          a = dot2(d.w23, xcd, a);
-          a = dot2(d.w45, xef, a);
-          a = dot2(d.w67, xgh, a);
-          acc[b] = a;
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < BMAX; ++b) tot[b] = __builtin_fmaf(sf, acc[b], tot[b]);
-  }
-}
-
-// Stage x columns [col0, col0 + ncols) of every batch vector into LDS planes.
-template <int NK>
-__device__ __forceinline__ void stage_x(const KParams& p, u32x4* xs, int col0, int ncols, int ldsb,
-                                        int tid, int nthreads) {
-  constexpr int CPC = 128 / NK, BPC = CPC / 8, LSTRIDE = BPC + 1;
-  const int nblk = ncols >> 3;
-  const int kb = p.K >> 3;
-  for (int m = tid; m < p.B * nblk; m += nthreads) {
-    const int b = m / nblk, blk = m - b * nblk;
-    const int col = col0 + (blk << 3);
-    if (col < p.K) {
-      const u32x4 xv = p.x[b * kb + (col >> 3)];
-      u32x4 pl;
-      pl.x = perm_b32(xv.y, xv.x, 0x06040200u);  // low bytes of columns 0..3
-      pl.y = perm_b32(xv.w, xv.z, 0x06040200u);  // low bytes of columns 4..7
-      pl.z = perm_b32(xv.y, xv.x, 0x07050301u);  // high bytes of columns 0..3
-      pl.w = perm_b32(xv.w, xv.z, 0x07050301u);  // high bytes of columns 4..7
-      xs[b * ldsb + (blk / BPC) * LSTRIDE + (blk % BPC)] = pl;
-    }
-  }
-}
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
-}
-
-// Sum over groups of 2^tpr_log2 consecutive lanes with DPP; the group's last
-// lane ends up holding the group's total.
-__device__ __forceinline__ float row_reduce(float a, int tpr_log2) {
-  if (tpr_log2 >= 1) a += dpp_f32<0xB1, 0xF>(a);   // quad_perm [1,0,3,2]
-  if (tpr_log2 >= 2) a += dpp_f32<0x4E, 0xF>(a);   // quad_perm [2,3,0,1]
-  if (tpr_log2 >= 3) a += dpp_f32<0x141, 0xF>(a);  // row_half_mirror
-  if (tpr_log2 >= 4) a += dpp_f32<0x140, 0xF>(a);  // row_mirror
-  if (tpr_log2 >= 5) a += dpp_f32<0x142, 0xA>(a);  // row_bcast:15 into rows 1 and 3
-  if (tpr_log2 >= 6) a += dpp_f32<0x143, 0xC>(a);  // row_bcast:31 into rows 2 and 3
-  return a;
-}
-
-// Thread role inside a tile: the row r, its k-lane kl and how many chunks it owns.
-struct Role {
-  int r, kl, nch, I, rem, TPR;
-  bool active;
-};
-
-__device__ __forceinline__ Role make_role(const KParams& p, int vt, int nr) {
-  Role o;
-  o.TPR = 1 << p.tpr_log2;
-  o.r = vt >> p.tpr_log2;
-  o.kl = vt & (o.TPR - 1);
-  o.active = o.r < nr;
-  o.I = (p.C + o.TPR - 1) >> p.tpr_log2;
-  o.rem = p.C - (o.I - 1) * o.TPR;
-  o.nch = o.active ? (o.kl < o.rem ? o.I : o.I - 1) : 0;
-  return o;
-}
-
-// Loads of one chunk slot: codes, offsets and its scale|zero words.
-template <int SPC, int SHARE>
-__device__ __forceinline__ void load_chunk(const KParams& p, int64_t slot0, int s_rel, int sz_base,
-                                           u32x4& v, u32x2& o, uint32_t (&s)[SPC]) {
-  v = __builtin_nontemporal_load(p.vals + slot0 + s_rel);
-  o = __builtin_nontemporal_load(p.offs + slot0 + s_rel);
-  const uint32_t* sp = p.sz + sz_base + (SPC > 1 ? s_rel * SPC : s_rel / SHARE);
-  if constexpr (SPC == 4) {
-    const u32x4 w = __builtin_nontemporal_load((const u32x4*)sp);
-    s[0] = w.x; s[1] = w.y; s[2] = w.z; s[3] = w.w;
-  } else if constexpr (SPC == 2) {
-    const u32x2 w = __builtin_nontemporal_load((const u32x2*)sp);
-    s[0] = w.x; s[1] = w.y;
-  } else {
-    s[0] = __builtin_nontemporal_load(sp);
-  }
-}
-
-// One tile (or one pass of a tile) at batch <= BMAX with up to MAXCH chunks per lane.
-template <int NK, int G, int BMAX, int MAXCH>
-__device__ __forceinline__ void tile_body(const KParams& p, u32x4* xs, int row0, int nr, int sz_base, int vt) {
-  constexpr int CPC = 128 / NK;
-  constexpr int LSTRIDE = CPC / 8 + 1;
-  constexpr int SPC = (G >= CPC) ? 1 : CPC / G;   // scale words per chunk
-  constexpr int SHARE = (G > CPC) ? G / CPC : 1;  // chunks per scale word
-  const Role ro = make_role(p, vt, nr);
-  const int64_t slot0 = (int64_t)row0 * p.C;
-  Consts k;
-  k.magic = 0x64006400u;
-  k.sel_or = NK == 2 ? 0x04040000u : 0x04000400u;
-
-  const int yrow = p.perm[row0 + (ro.active ? ro.r : 0)];
-  u32x4 v[MAXCH];
-  u32x2 o[MAXCH];
-  uint32_t s[MAXCH][SPC];
-#pragma unroll
-  for (int i = 0; i < MAXCH; ++i) {
-    if (i < ro.nch) {
-      const int cnt = (i == ro.I - 1) ? ro.rem : ro.TPR;
-      load_chunk<SPC, SHARE>(p, slot0, i * nr * ro.TPR + ro.r * cnt + ro.kl, sz_base, v[i], o[i], s[i]);
-    }
-  }
-
-  const int PI = p.phase_iters;
-  const int ldsb = PI * ro.TPR * LSTRIDE;  // LDS blocks per batch vector
-  const int phase_cols = PI * ro.TPR * CPC;
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  stage_x<NK>(p, xs, 0, phase_cols, ldsb, tid, nthr);
-  __syncthreads();
-
-  float tot[BMAX];
-#pragma unroll
-  for (int b = 0; b < BMAX; ++b) tot[b] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < MAXCH; ++i) {
-    const int ip = (MAXCH == 1) ? 0 : i % PI;
-    if (MAXCH > 1 && i > 0 && ip == 0 && i < ro.I) {  // uniform across the workgroup
-      __syncthreads();
-      stage_x<NK>(p, xs, (i / PI) * phase_cols, phase_cols, ldsb, tid, nthr);
-      __syncthreads();
-    }
-    if (i < ro.nch) {
-      const u32x4* xc = xs + (ip * ro.TPR + ro.kl) * LSTRIDE;
-      chunk_compute<NK, G, BMAX, SPC>(v[i], o[i], s[i], xc, ldsb, p.B, tot, k);
-    }
-  }
-
-#pragma unroll
-  for (int b = 0; b < BMAX; ++b) {
-    if (BMAX == 1 || b < p.B) {
-      const float a = row_reduce(tot[b], p.tpr_log2);
-      if (ro.active && ro.kl == ro.TPR - 1) p.y[(int64_t)b * p.N + yrow] = __builtin_bit_cast(uint16_t, (_Float16)a);
-    }
-  }
-}
 
 // Raw buffer loads: 32-bit lane offsets from a per-workgroup base held in
 // SGPRs; offsets at or beyond the range return zeros without touching memory.
@@ -337,163 +72,226 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 // CPOL: 0 = default caching, 2 = non-temporal (the weights are read once).
 constexpr int kCached = 0, kStream = 2;
-template <int CPOL = kCached>
+template <int CPOL>
 __device__ __forceinline__ u32x4 bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL));
 }
-template <int CPOL = kCached>
+template <int CPOL>
 __device__ __forceinline__ u32x2 bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CPOL));
 }
-template <int CPOL = kCached>
+template <int CPOL>
 __device__ __forceinline__ uint32_t bload1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CPOL);
 }
 
-// Batch-1 tile. A workgroup of nthr lanes covers rt = RPL * nthr / tpr rows:
-// lane (lane_row, kl) handles rows lane_row + j * nthr / tpr, j < RPL, and
-// chunks kl, kl + tpr, ... (< IMAX per row) of each. x is staged once per
-// workgroup; its loads are issued before the weight loads so that the LDS
-// staging and the barrier do not wait for the weights (vector loads complete
-// in issue order). Every load is unconditional (lanes without work read out
-// of range and get zeros), so the number of loads in flight is static and
-// each chunk is consumed as soon as its own loads have landed.
-template <int NK, int G, int RPL, int IMAX, int XMAX>
-__device__ __forceinline__ void tile_b1(const KParams& p, u32x4* xs, int row0, int nr, int sz_base) {
-  constexpr int CPC = 128 / NK, BPC = CPC / 8, LSTRIDE = BPC + 1;
-  constexpr int SPC = (G >= CPC) ? 1 : CPC / G;
-  constexpr int SHARE = (G > CPC) ? G / CPC : 1;
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  const int tl = p.tpr_log2, TPR = 1 << tl;
-  const int lane_row = tid >> tl, kl = tid & (TPR - 1);
-  const int rows_per_pass = nthr >> tl;
-  const int C = p.C;
-  const int I = (C + TPR - 1) >> tl;
-  const int rem = C - (I - 1) * TPR;
-  Consts k;
-  k.magic = 0x64006400u;
-  k.sel_or = NK == 2 ? 0x04040000u : 0x04000400u;
+// A VGPR holding c whose value the compiler cannot see, so that (a & m) | c
+// becomes one v_and_or_b32 (m in an SGPR, c in this VGPR). A single VALU move
+// at kernel start, before any matrix-core instruction.
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+  return r;
+}
 
-  // per-workgroup buffer windows
-  const uint32_t tile_slots = (uint32_t)nr * (uint32_t)C;
-  const int64_t slot0 = (int64_t)row0 * C;
-  const auto rx = make_rsrc(p.x, (uint32_t)p.K * 2u);
-  const auto rv = make_rsrc(p.vals + slot0, tile_slots * 16u);
-  const auto ro = make_rsrc(p.offs + slot0, tile_slots * 8u);
-  const auto rs = make_rsrc(p.sz + sz_base, tile_slots * (uint32_t)CPC / (uint32_t)G * 4u);
-  const auto rp = make_rsrc(p.perm + row0, (uint32_t)nr * 4u);
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 
-  // 1. x loads (16 bytes = 8 columns each)
-  const int nblk = p.K >> 3;
+template <int ABID>
+__device__ __forceinline__ f4 smfmac(h8 a, h16 b, f4 c, uint32_t idx) {
+  return __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, b, c, (int)idx, 0, ABID);
+}
+
+// Per-lane constants of one scale|zero word: (s, s), -(1024 + z), -(64 + z).
+struct Deq { h2 s, c1, c16; };
+__device__ __forceinline__ Deq deq_consts(uint32_t szw) {
+  const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
+  const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)(szw >> 16));
+  const _Float16 a = (_Float16)-1024.0f - z, b = (_Float16)-64.0f - z;   // exact: integers <= 1039
+  Deq d;
+  d.s = h2{s, s};
+  d.c1 = h2{a, a};
+  d.c16 = h2{b, b};
+  return d;
+}
+
+// FP16 pairs (q0 - z) * s, (q1 - z) * s of two nibbles placed by the mask:
+// 0x000F000F gives 1024 + q (subtract 1024 + z); 0x00F000F0 gives 1024 + 16 q
+// (times 1/16, subtract 64 + z). (q - z) is exact; the product is rounded once.
+__device__ __forceinline__ uint32_t deq_lo(uint32_t w, uint32_t magic, const Deq& d) {
+  return as_u32((as_h2((w & 0x000F000Fu) | magic) + d.c1) * d.s);
+}
+__device__ __forceinline__ uint32_t deq_hi(uint32_t w, uint32_t magic, const Deq& d) {
+  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  return as_u32(__builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | magic), sixteenth, d.c16) * d.s);
+}
+
+// Number of scale|zero words per column chunk of the sorted rows before row
+// i: sum over classes k of (256 / (32 << k)) * (rows of class k before i).
+__device__ __forceinline__ int words_before(const KParams& p, int i) {
+  int s = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int n = i - p.cls_row[k];
+    n = n < 0 ? 0 : n;
+    const int nk = p.cls_row[k + 1] - p.cls_row[k];
+    s += (8 >> k) * (n < nk ? n : nk);
+  }
+  return s;
+}
+
+template <int NK, int IMAX, int XMAX>
+__global__ __launch_bounds__(1024) void sgemv_kernel(KParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int rb = blockIdx.x;
+  if (rb >= p.T) return;
+  constexpr int CB = 8 * NK, OB = 4 * NK;   // bytes of one piece's codes and offsets
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, W = blockDim.x >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int B = p.B, PH = p.phase;
+  const auto rbuf = make_rsrc(p.blob, p.blob_bytes);
+  const auto rx = make_rsrc(p.x, (uint32_t)(B * p.K * 2));
+  const int c0 = w * p.cpw;
+  const int ncw = p.C - c0 < p.cpw ? (p.C - c0 > 0 ? p.C - c0 : 0) : p.cpw;   // chunks of this wave
+
+  // this lane's sorted row, its group size 32 << cls and its scale|zero words
+  const int row = rb * 16 + r;
+  const bool row_ok = row < p.N;
+  const int cls = (row >= p.cls_row[1]) + (row >= p.cls_row[2]) + (row >= p.cls_row[3]);
+  const int glog = 5 + cls;
+  const int wb0 = words_before(p, rb * 16);
+  const uint32_t rec_words = (uint32_t)(words_before(p, rb * 16 + 16) - wb0);
+  const uint32_t sz_lane = (uint32_t)(words_before(p, row) - wb0) + (uint32_t)((64 * q) >> glog);
+  const uint32_t sz_block = (uint32_t)wb0 * (uint32_t)p.C;
+  const bool g32 = cls == 0;
+
+  // 0. original index of row tid % 16 of the block, for the lanes that write y
+  const uint32_t orow = bload1<kCached>(rbuf, p.off_perm + (uint32_t)(rb * 16 + (tid & 15)) * 4u);
+
+  // 1. x slice of the first phase: B rows x (PH * 256) columns, 16 bytes per load
+  const int span16 = PH * 32;
   u32x4 xv[XMAX];
+  auto issue_x = [&](int first) {   // chunks c0 + first .. c0 + first + PH - 1
+    const int lim = (ncw - first < PH ? ncw - first : PH) * 32;
 #pragma unroll
-  for (int j = 0; j < XMAX; ++j) xv[j] = bload4(rx, (uint32_t)(tid + j * nthr) * 16u);
-  __builtin_amdgcn_sched_barrier(0);
-  // 2. row indices and weight loads
-  uint32_t yrow[RPL];
-  bool has[RPL][IMAX];
-  u32x4 v[RPL][IMAX];
-  u32x2 o[RPL][IMAX];
-  uint32_t s[RPL][IMAX][SPC];
-#pragma unroll
-  for (int j = 0; j < RPL; ++j) {
-    const int r = lane_row + j * rows_per_pass;
-    const bool row_ok = r < nr;
-    yrow[j] = bload1(rp, row_ok ? (uint32_t)r * 4u : kOutOfRange);
-#pragma unroll
-    for (int i = 0; i < IMAX; ++i) {
-      const bool ok = row_ok && (i < I - 1 || (i == I - 1 && kl < rem));
-      has[j][i] = ok;
-      const int cnt = (i == I - 1) ? rem : TPR;
-      const uint32_t s_rel = (uint32_t)(i * nr * TPR + r * cnt + kl);
-      v[j][i] = bload4<kStream>(rv, ok ? s_rel * 16u : kOutOfRange);
-      o[j][i] = bload2<kStream>(ro, ok ? s_rel * 8u : kOutOfRange);
-      const uint32_t soff = ok ? (SPC > 1 ? s_rel * SPC : s_rel / SHARE) * 4u : kOutOfRange;
-      if constexpr (SPC == 4) {
-        const u32x4 w = bload4<kStream>(rs, soff);
-        s[j][i][0] = w.x; s[j][i][1] = w.y; s[j][i][2] = w.z; s[j][i][3] = w.w;
-      } else if constexpr (SPC == 2) {
-        const u32x2 w = bload2<kStream>(rs, soff);
-        s[j][i][0] = w.x; s[j][i][1] = w.y;
-      } else {
-        s[j][i][0] = bload1<kStream>(rs, soff);
-      }
+    for (int j = 0; j < XMAX; ++j) {
+      const int u = lane + 64 * j, b = u / span16, cu = u - b * span16;
+      const bool ok = b < B && cu < lim;
+      xv[j] = bload4<kCached>(rx, ok ? (uint32_t)(b * p.K + (c0 + first) * 256 + cu * 8) * 2u : kOutOfRange);
     }
+  };
+  issue_x(0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // weights of every chunk of the wave
+  typedef typename std::conditional<NK == 2, u32x4, u32x2>::type CodeT;
+  typedef typename std::conditional<NK == 2, u32x2, uint32_t>::type OffT;
+  CodeT cv[IMAX];
+  OffT ov[IMAX];
+  u32x2 sv[IMAX];
+#pragma unroll
+  for (int i = 0; i < IMAX; ++i) {
+    const int c = c0 + i;
+    const bool ok = i < ncw;
+    const uint32_t rec = (uint32_t)(rb * p.C + c) * 64u + lane;
+    const uint32_t so = p.off_sz + (sz_block + (uint32_t)c * rec_words + sz_lane) * 4u;
+    if constexpr (NK == 2) {
+      cv[i] = bload4<kStream>(rbuf, ok ? p.off_codes + rec * CB : kOutOfRange);
+      ov[i] = bload2<kStream>(rbuf, ok ? p.off_offs + rec * OB : kOutOfRange);
+    } else {
+      cv[i] = bload2<kStream>(rbuf, ok ? p.off_codes + rec * CB : kOutOfRange);
+      ov[i] = bload1<kStream>(rbuf, ok ? p.off_offs + rec * OB : kOutOfRange);
+    }
+    sv[i] = bload2<kStream>(rbuf, ok && row_ok ? so : kOutOfRange);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // 3. x planes into LDS (low bytes of 8 columns, then their high bytes)
+
+  _Float16* xs = reinterpret_cast<_Float16*>(smem) + w * (B * span16 * 8);
+  float* part = reinterpret_cast<float*>(smem + W * B * span16 * 16);
+  const uint32_t magic = opaque_vgpr(0x64006400u);
+  const int bcol = (lane & 15) < B ? (lane & 15) : 0;
+  const _Float16* xrow = xs + bcol * (span16 * 8) + 64 * (q >> 1) + 8 * (q & 1);
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+
 #pragma unroll
-  for (int j = 0; j < XMAX; ++j) {
-    const int m = tid + j * nthr;
-    if (XMAX == 1 || m < nblk) {
-      u32x4 pl;
-      pl.x = perm_b32(xv[j].y, xv[j].x, 0x06040200u);
-      pl.y = perm_b32(xv[j].w, xv[j].z, 0x06040200u);
-      pl.z = perm_b32(xv[j].y, xv[j].x, 0x07050301u);
-      pl.w = perm_b32(xv[j].w, xv[j].z, 0x07050301u);
-      xs[(m / BPC) * LSTRIDE + (m % BPC)] = pl;
+  for (int i = 0; i < IMAX; ++i) {
+    if (i >= ncw) break;
+    const int slot = i % PH;
+    if (slot == 0) {
+      // 2. stage this phase's x slice in the wave's LDS region, prefetch the next
+#pragma unroll
+      for (int j = 0; j < XMAX; ++j) {
+        const int u = lane + 64 * j;
+        if (u < B * span16) reinterpret_cast<u32x4*>(xs)[u] = xv[j];
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (i + PH < ncw) issue_x(i + PH);
     }
+    const _Float16* xc = xrow + 256 * slot;
+    // scale|zero of columns 0..31 and 32..63 of this lane's piece (two groups
+    // at group size 32, one otherwise)
+    const Deq d0 = deq_consts(sv[i].x);
+    const Deq d1 = deq_consts(g32 ? sv[i].y : sv[i].x);
+    uint32_t idx2 = 0;
+    if constexpr (NK == 1) idx2 = ((ov[i] & 0x33333333u) << 2) | ((ov[i] >> 2) & 0x33333333u);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const Deq& d = t < 2 ? d0 : d1;
+      uint32_t a0, a1, a2, a3, idx;
+      if constexpr (NK == 2) {
+        // step t: code dword t = 8 kept elements, 2 per group of 4 columns
+        const uint32_t cw = cv[i][t], c8 = cw >> 8;
+        a0 = deq_lo(cw, magic, d);
+        a1 = deq_hi(cw, magic, d);
+        a2 = deq_lo(c8, magic, d);
+        a3 = deq_hi(c8, magic, d);
+        idx = ov[i][t >> 1];
+      } else {
+        // step t: 4 kept elements (one per group) in slots 0, 2, 5, 7; the
+        // other slot of each group holds 0
+        const uint32_t cw = (t & 1) ? (cv[i][t >> 1] >> 8) : cv[i][t >> 1];
+        const uint32_t v02 = deq_lo(cw, magic, d), v13 = deq_hi(cw, magic, d);
+        a0 = v02 & 0x0000FFFFu;
+        a2 = v02 & 0xFFFF0000u;
+        a1 = v13 & 0x0000FFFFu;
+        a3 = v13 & 0xFFFF0000u;
+        idx = t < 2 ? ov[i] : idx2;
+      }
+      const h2 A0 = as_h2(a0), A1 = as_h2(a1), A2 = as_h2(a2), A3 = as_h2(a3);
+      const h8 A = {A0.x, A0.y, A1.x, A1.y, A2.x, A2.y, A3.x, A3.y};
+      const h8 blo = *reinterpret_cast<const h8*>(xc + 16 * t);
+      const h8 bhi = *reinterpret_cast<const h8*>(xc + 16 * t + 128);
+      const h16 Bop = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      if (t & 1) acc = smfmac<1>(A, Bop, acc, idx);
+      else acc = smfmac<0>(A, Bop, acc, idx);
+    }
+  }
+
+  // 4. partial sums of the waves: part[b][row][wave]; lane (b = lane % 16,
+  // q) holds rows 4q .. 4q + 3 of column b
+  if ((lane & 15) < B) {
+    float* pp = part + ((lane & 15) * 16 + 4 * q) * 16 + w;
+    pp[0] = acc.x;
+    pp[16] = acc.y;
+    pp[32] = acc.z;
+    pp[48] = acc.w;
   }
   __syncthreads();
-  // 4. compute row by row, chunk by chunk as the loads land
+  // entries e = 16 b + row; the block size is a multiple of 16, so every
+  // entry of this lane has row tid % 16
+  for (int e = tid; e < 16 * B; e += blockDim.x) {
+    const int b = e >> 4, rr = e & 15;
+    const f4* pv = reinterpret_cast<const f4*>(part + (b * 16 + rr) * 16);
+    const f4 v0 = pv[0], v1 = pv[1], v2 = pv[2], v3 = pv[3];
+    const float vv[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
+                          v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+    float s = 0.f;
 #pragma unroll
-  for (int j = 0; j < RPL; ++j) {
-    const int r = lane_row + j * rows_per_pass;
-    float tot[1] = {0.0f};
-#pragma unroll
-    for (int i = 0; i < IMAX; ++i) {
-      if (has[j][i]) {   // the LDS beyond the last chunk's columns holds no x
-        const u32x4* xc = xs + (i * TPR + kl) * LSTRIDE;
-        chunk_compute<NK, G, 1, SPC>(v[j][i], o[j][i], s[j][i], xc, 0, 1, tot, k);
-      }
-    }
-    const float a = row_reduce(tot[0], tl);
-    if (r < nr && kl == TPR - 1) p.y[yrow[j]] = __builtin_bit_cast(uint16_t, (_Float16)a);
+    for (int v = 0; v < 16; ++v)
+      if (v < W) s += vv[v];
+    const int n = (int)orow;
+    if (n >= 0 && n < p.N) p.y[(int64_t)b * p.N + n] = __builtin_bit_cast(uint16_t, (_Float16)s);
   }
 }
-
-// Batch-1 kernel: one workgroup per tile.
-template <int NK, int RPL, int IMAX, int XMAX>
-__global__ __launch_bounds__(256) void sgemv_b1_kernel(KParams p) {
-  extern __shared__ u32x4 xs[];
-  if ((int)blockIdx.x >= p.cls_tile[4]) return;   // no such tile (uniform per workgroup)
-  const TileGeo t = tile_geo(p, blockIdx.x);
-  switch (t.g) {
-    case 32: tile_b1<NK, 32, RPL, IMAX, XMAX>(p, xs, t.row0, t.nr, t.sz_base); break;
-    case 64: tile_b1<NK, 64, RPL, IMAX, XMAX>(p, xs, t.row0, t.nr, t.sz_base); break;
-    case 128: tile_b1<NK, 128, RPL, IMAX, XMAX>(p, xs, t.row0, t.nr, t.sz_base); break;
-    default: tile_b1<NK, 256, RPL, IMAX, XMAX>(p, xs, t.row0, t.nr, t.sz_base); break;
-  }
-}
-
-// Beam-batch kernel (B = 2..16): 256-thread workgroups; a tile whose layout
-// uses more threads is split into 1 << pass_log2 workgroups, each taking a
-// contiguous block of the tile's (row, k-lane) slots. Batch vectors are taken
-// 4 at a time so that their x planes fit in LDS; each group of 4 re-reads
-// the workgroup's weights, which are then still in L2.
-template <int NK>
-__global__ __launch_bounds__(256) void sgemv_bn_kernel(KParams p) {
-  extern __shared__ u32x4 xs[];
-  const int pass = blockIdx.x & ((1 << p.pass_log2) - 1);
-  if ((int)(blockIdx.x >> p.pass_log2) >= p.cls_tile[4]) return;   // no such tile
-  const TileGeo t = tile_geo(p, blockIdx.x >> p.pass_log2);
-  const int row0 = t.row0, nr = t.nr, g = t.g, sz_base = t.sz_base;
-  const int vt = threadIdx.x + 256 * pass;
-  for (int b0 = 0; b0 < p.B; b0 += 4) {
-    KParams q = p;
-    q.x = p.x + (int64_t)b0 * (p.K >> 3);
-    q.y = p.y + (int64_t)b0 * p.N;
-    q.B = p.B - b0 < 4 ? p.B - b0 : 4;
-    if (b0 > 0) __syncthreads();
-    switch (g) {
-      case 32: tile_body<NK, 32, 4, 8>(q, xs, row0, nr, sz_base, vt); break;
-      case 64: tile_body<NK, 64, 4, 8>(q, xs, row0, nr, sz_base, vt); break;
-      case 128: tile_body<NK, 128, 4, 8>(q, xs, row0, nr, sz_base, vt); break;
-      default: tile_body<NK, 256, 4, 8>(q, xs, row0, nr, sz_base, vt); break;
-    }
-  }
-}
-
-typedef void (*KernelFn)(KParams);
 
 }  // namespace sgemv_dev

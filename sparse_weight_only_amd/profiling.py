@@ -101,11 +101,8 @@ def _bench_layer_kernels() -> dict:
         gs = sg.select_groups(W, L.nk, L.Xcal(synth.CALIB_T), synth.FRAC_FINE, synth.G_FINE, synth.G_COARSE)
         d = sg.describe(L.N, L.K, L.nk, gs)
         pl = sg.plan(d, 1)
-        C = L.K * L.nk // 128
-        iters = -(-C // d.tpr)
-        imax = 1 if iters <= 1 else 2 if iters <= 2 else 4 if iters <= 4 else 8
-        xmax = 2 if -(-(L.K // 8) // pl.block) <= 2 else 8
-        name = f"sgemv_b1_kernel<{L.nk}, {pl.rows_per_lane}, {imax}, {xmax}>"
+        bucket = lambda n: 1 if n <= 1 else 2 if n <= 2 else 4 if n <= 4 else 8
+        name = f"sgemv_kernel<{L.nk}, {bucket(pl.chunks_per_wave)}, {bucket(pl.x_loads)}>"
         res[L.name] = (name, int(pl.grid * pl.block))
     return res
 

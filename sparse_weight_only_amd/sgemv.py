@@ -34,13 +34,12 @@ class SgemvError(RuntimeError):
 class Desc(ctypes.Structure):
     _fields_ = [
         ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("nk", ctypes.c_int32),
-        ("rt", ctypes.c_int32), ("tpr", ctypes.c_int32), ("n_tiles", ctypes.c_int32),
+        ("n_blocks", ctypes.c_int32), ("chunks", ctypes.c_int32),
         ("g_min", ctypes.c_int32), ("g_max", ctypes.c_int32),
         ("class_rows", ctypes.c_int32 * 4), ("reserved", ctypes.c_int32),
         ("kept", ctypes.c_int64), ("vals_bytes", ctypes.c_int64), ("offs_bytes", ctypes.c_int64),
-        ("n_groups", ctypes.c_int64), ("off_tiles", ctypes.c_int64), ("off_perm", ctypes.c_int64),
-        ("off_vals", ctypes.c_int64), ("off_offs", ctypes.c_int64), ("off_sz", ctypes.c_int64),
-        ("blob_bytes", ctypes.c_int64),
+        ("n_groups", ctypes.c_int64), ("off_codes", ctypes.c_int64), ("off_offs", ctypes.c_int64),
+        ("off_perm", ctypes.c_int64), ("off_sz", ctypes.c_int64), ("blob_bytes", ctypes.c_int64),
     ]
 
     def as_dict(self) -> dict:
@@ -50,8 +49,8 @@ class Desc(ctypes.Structure):
 class Plan(ctypes.Structure):
     _fields_ = [
         ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int64), ("block", ctypes.c_int32),
-        ("pass_log2", ctypes.c_int32), ("rows_per_lane", ctypes.c_int32),
-        ("chunks_per_row_lane", ctypes.c_int32), ("phase_iters", ctypes.c_int32), ("batched", ctypes.c_int32),
+        ("waves", ctypes.c_int32), ("chunks_per_wave", ctypes.c_int32), ("phase_chunks", ctypes.c_int32),
+        ("x_loads", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:
@@ -72,7 +71,7 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
-        L.sgemv_describe.argtypes = [i32, i32, i32, P, i32, i32, ctypes.POINTER(Desc)]
+        L.sgemv_describe.argtypes = [i32, i32, i32, P, ctypes.POINTER(Desc)]
         L.sgemv_select_groups.argtypes = [P, i32, i32, i32, P, i32, f64, i32, i32, P]
         L.sgemv_pack.argtypes = [P, i32, i32, i32, P, P, P, P, P, P, P]
         L.sgemv_layout.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P, P]
@@ -106,10 +105,12 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
-def describe(N: int, K: int, nk: int, group_size, rt: int = 0, tpr: int = 0) -> Desc:
+def describe(N: int, K: int, nk: int, group_size) -> Desc:
     gs = _host(np.asarray(group_size, dtype=np.int32), np.int32)
+    if gs.shape != (N,):
+        raise ValueError("group_size must have one entry per row")
     d = Desc()
-    _check(lib().sgemv_describe(N, K, nk, _ptr(gs), rt, tpr, ctypes.byref(d)), "sgemv_describe")
+    _check(lib().sgemv_describe(N, K, nk, _ptr(gs), ctypes.byref(d)), "sgemv_describe")
     return d
 
 
@@ -190,7 +191,7 @@ class SparseGemvLayer:
     @classmethod
     def from_dense(cls, w16: np.ndarray, nk: int, group_size=None, xcal16: Optional[np.ndarray] = None,
                    frac_fine: float = 0.10, g_fine: int = 32, g_coarse: int = 128,
-                   rt: int = 0, tpr: int = 0, device="cuda") -> "SparseGemvLayer":
+                   device="cuda") -> "SparseGemvLayer":
         w16 = np.asarray(w16, dtype=np.float16)
         N, K = w16.shape
         if group_size is None:
@@ -200,7 +201,7 @@ class SparseGemvLayer:
                 raise ValueError("adaptive groups need a calibration batch")
             group_size = select_groups(w16, nk, xcal16, frac_fine, g_fine, g_coarse)
         canon = pack(w16, nk, group_size)
-        desc = describe(N, K, nk, group_size, rt, tpr)
+        desc = describe(N, K, nk, group_size)
         return cls(desc, canon, layout(desc, canon), device)
 
     def run(self, x, y=None, stream=None):

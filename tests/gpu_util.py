@@ -21,8 +21,8 @@ def group_sizes(L, W):
     return sg.select_groups(W, L.nk, L.Xcal(synth.CALIB_T), synth.FRAC_FINE, synth.G_FINE, synth.G_COARSE)
 
 
-def make_layer(W, nk, gs, rt=0, tpr=0):
-    return sg.SparseGemvLayer.from_dense(W, nk, np.asarray(gs, np.int32), rt=rt, tpr=tpr)
+def make_layer(W, nk, gs):
+    return sg.SparseGemvLayer.from_dense(W, nk, np.asarray(gs, np.int32))
 
 
 def run_checked(layer, X16, guard=64):

@@ -34,27 +34,23 @@ def grid_weights(N, K, nk, g, rng, s=2.0 ** -6):
 
 
 @pytest.mark.parametrize("nk", [2, 1])
-@pytest.mark.parametrize("N,K,gs_kind,rt,tpr", [
-    (1024, 1024, "u128", 0, 0), (300, 4096, "mixed", 0, 0), (77, 11008, "mixed", 0, 0),
-    (513, 2048, "all", 16, 16), (40, 768, "mixed", 2, 32), (1, 256, "u128", 0, 0),
-    (130, 1280, "all", 1, 64), (96, 512, "u32", 64, 4),
+@pytest.mark.parametrize("N,K,gs_kind", [
+    (1024, 1024, "u128"), (300, 4096, "mixed"), (77, 11008, "mixed"), (513, 2048, "all"),
+    (40, 768, "mixed"), (1, 256, "u128"), (130, 1280, "all"), (96, 512, "u32"), (17, 32768, "all"),
 ])
-def test_exact_arithmetic_bit_exact(nk, N, K, gs_kind, rt, tpr):
+def test_exact_arithmetic_bit_exact(nk, N, K, gs_kind):
     rng = np.random.default_rng(N + K + nk)
     gchoices = {"u128": [128], "u32": [32], "mixed": [32, 128], "all": [32, 64, 128, 256]}[gs_kind]
-    gchoices = [g for g in gchoices if K % g == 0]
     gs = rng.choice(gchoices, N).astype(np.int32)
-    if tpr and max(gs) > 128 // nk and (tpr % (max(gs) // (128 // nk))):
-        gs = np.minimum(gs, 128)
     W = np.zeros((N, K), np.float16)
     for g in np.unique(gs):
         rows = gs == g
         W[rows] = grid_weights(int(rows.sum()), K, nk, int(g), rng)
-    say(f"case exact nk={nk} N={N} K={K} groups={gs_kind} rt={rt} tpr={tpr}")
-    layer = make_layer(W, nk, gs, rt, tpr)
+    say(f"case exact nk={nk} N={N} K={K} groups={gs_kind}")
+    layer = make_layer(W, nk, gs)
     co = check_pack_matches_oracle(W, nk, gs, layer.canon)
     assert np.all(np.abs(co["scale"].view(np.float16).astype(np.float64) - 2.0 ** -6) == 0)
-    for B in (1, 3):
+    for B in (1, 3, 16):
         X = np.zeros((B, K), np.float16)
         for b in range(B):
             idx = rng.choice(K, size=min(64, K), replace=False)
@@ -161,3 +157,23 @@ def test_zero_input_gives_zero_output():
     layer = make_layer(W, 2, np.full(64, 128, np.int32))
     y = run_checked(layer, np.zeros((2, 512), np.float16))
     assert np.all(y.view(np.uint16) == 0)
+
+
+@pytest.mark.parametrize("nk", [2, 1])
+@pytest.mark.parametrize("N,K", [(16, 256), (600, 8192), (40, 11008), (17, 32768)])
+def test_every_launch_geometry(nk, N, K):
+    """Shapes and batches that together launch every reachable kernel instance
+    (chunks per wave 1..8, x loads per lane 1..8, phased staging of x)."""
+    rng = np.random.default_rng(N + nk)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    gs = rng.choice([32, 64, 128, 256], N).astype(np.int32)
+    layer = make_layer(W, nk, gs)
+    for B in (1, 2, 3, 4, 8, 16):
+        pl = sg.plan(layer.desc, B)
+        say(f"case geometry N={N} K={K} nk={nk} B={B} waves={pl.waves} cpw={pl.chunks_per_wave} "
+            f"phase={pl.phase_chunks} xloads={pl.x_loads}")
+        X = rng.standard_normal((B, K)).astype(np.float16)
+        y = run_checked(layer, X)
+        y_ref, D, _ = oracle_y(layer.canon, X)
+        err = ogemv.normalized_error(y, y_ref, D)
+        assert err <= TOL, (B, err)

@@ -1,4 +1,5 @@
-"""Pins oracle.layout: hand-placed bytes and decode(build(.)) == identity."""
+"""Pins oracle.layout: hand-placed bytes, row order, record order and
+decode(build(.)) == identity over ragged and mixed-class shapes."""
 import numpy as np
 import pytest
 
@@ -22,8 +23,12 @@ def synthetic_canon(N, K, nk, gs, seed=0):
             "gptr": gptr.astype(np.int32)}, q, o
 
 
-def test_hand_placed_bytes():
-    N, K, nk = 2, 256, 2                      # C = 4 chunks per row
+def u32_at(blob, at):
+    return int.from_bytes(blob[at: at + 4].tobytes(), "little")
+
+
+def test_hand_placed_bytes_2of4():
+    N, K, nk = 2, 256, 2                      # one row block, one column chunk
     kpr = K * nk // 4
     q = np.array([[(j + n) % 16 for j in range(kpr)] for n in range(N)], dtype=np.uint8)
     o = np.array([[j % 4 for j in range(kpr)] for n in range(N)], dtype=np.uint8)
@@ -33,57 +38,107 @@ def test_hand_placed_bytes():
              "scale": np.array([0x1111, 0x2222, 0x3333, 0x4444], np.uint16),
              "zero": np.array([0xAAAA, 0xBBBB, 0xCCCC, 0xDDDD], np.uint16),
              "gptr": np.array([0, 2, 4], np.int32)}
-    L = layout.build(canon, RT=2, TPR=4)
-    # one tile, one iteration: chunk c of row r sits at slot r*4 + c
-    # slot 0, dword 0 = elements 0..7 of row 0 (codes 0..7); nibble k holds
-    # element [0,2,4,6,1,3,5,7][k] -> 0x75316420
-    assert L["vals"][0][:4].tolist() == [0x20, 0x64, 0x31, 0x75]
-    # slot 5 = row 1, chunk 1: elements 32..39 of row 1 have codes (j+1)%16 = 1..8
-    # nibbles [1,3,5,7,2,4,6,8] -> 0x86427531
-    assert L["vals"][5][:4].tolist() == [0x31, 0x75, 0x42, 0x86]
-    # offsets j%4: element 4q+b at bits 8b+2q -> byte b = b*0x55
-    assert L["offs"][0].tolist() == [0x00, 0x55, 0xAA, 0xFF] * 2
-    # group 128 covers two 64-column chunks at 2:4: slots (0,1) share entry 0
-    assert L["sz"].tolist() == [0xAAAA1111, 0xBBBB2222, 0xCCCC3333, 0xDDDD4444]
-    assert L["tiles"].tolist() == [[0, 2, 128, 0]]
-    assert L["perm"].tolist() == [0, 1]
+    L = layout.build(canon)
     off = L["offsets"]
-    assert off["perm"] == 256 and off["vals"] == 512 and off["offs"] == 512 + 256
-    assert off["sz"] == 512 + 256 + 256 and off["blob_bytes"] == 1280
+    # records of 64 lanes x 16 bytes: 1024 bytes of codes, then 512 of offsets,
+    # 64 of perm (16 rows) and 4 words + 8 spare bytes of scale|zero
+    assert (off["codes"], off["offs"], off["perm"], off["sz"], off["blob_bytes"]) == (0, 1024, 1536, 1792, 2048)
+    blob = L["blob"]
+    # lane 0 = row 0, columns 0..63 = kept elements 0..31; dword 0 = elements
+    # 0..7 (codes 0..7) with element k at nibble [0,4,1,5,2,6,3,7][k]:
+    # nibbles 0..7 hold 0,2,4,6,1,3,5,7 -> 0x75316420
+    assert u32_at(blob, 0) == 0x75316420
+    # lane 17 = row 1, columns 64..127 = elements 32..63; dword 0 = elements
+    # 32..39 with codes (j+1)%16 = 1..8 -> nibbles 1,3,5,7,2,4,6,8 -> 0x86427531
+    assert u32_at(blob, 17 * 16) == 0x86427531
+    # lane 48 = row 0, columns 192..255 = elements 96..127; dword 3 = elements
+    # 120..127, codes 8..15 -> nibbles 8,10,12,14,9,11,13,15 -> 0xFDB9ECA8
+    assert u32_at(blob, 48 * 16 + 12) == 0xFDB9ECA8
+    # offsets at 2:4 are the canonical bytes: offsets 0,1,2,3 at bits 0,2,4,6 -> 0xE4
+    assert blob[1024: 1024 + 8].tolist() == [0xE4] * 8
+    assert np.frombuffer(blob[1536: 1600].tobytes(), "<i4").tolist() == [0, 1] + [-1] * 14
+    # one record: row 0 with its 2 words of chunk 0, then row 1 with its 2
+    assert [u32_at(blob, 1792 + 4 * i) for i in range(4)] == [0xAAAA1111, 0xBBBB2222, 0xCCCC3333, 0xDDDD4444]
+    assert blob[1808: 2048].tolist() == [0] * 240
 
 
-def test_hand_ragged_slot():
-    # K=768 at 2:4 -> C = 12; TPR = 8 -> iterations of 8 and 4 chunks
-    N, K, nk = 2, 768, 2
-    canon, q, o = synthetic_canon(N, K, nk, [128, 128], seed=4)
-    L = layout.build(canon, RT=2, TPR=8)
-    # row 1, chunk 9 -> i = 1, kl = 1, cnt = 4 -> slot 1*2*8 + 1*4 + 1 = 21
-    e = 32 * 9 + np.array([0, 2, 4, 6, 1, 3, 5, 7])
-    want = sum(int(q[1, e[k]]) << (4 * k) for k in range(8))
-    got = int.from_bytes(L["vals"][21][:4].tobytes(), "little")
-    assert got == want
+def test_hand_placed_bytes_1of4():
+    N, K, nk = 1, 256, 1                      # 64 kept elements, 16 per piece
+    kpr = K * nk // 4
+    q = np.array([[j % 16 for j in range(kpr)]], dtype=np.uint8)
+    o = np.array([[(j // 4) % 4 for j in range(kpr)]], dtype=np.uint8)
+    vals, offs = pack.pack_bytes(q, o)
+    canon = {"N": N, "K": K, "nk": nk, "group_size": np.array([256], np.int32), "vals": vals, "offs": offs,
+             "scale": np.array([0x3C00], np.uint16), "zero": np.array([0x4800], np.uint16),
+             "gptr": np.array([0, 1], np.int32)}
+    L = layout.build(canon)
+    off = L["offsets"]
+    assert (off["codes"], off["offs"], off["perm"], off["sz"], off["blob_bytes"]) == (0, 512, 768, 1024, 1280)
+    blob = L["blob"]
+    # lane 16 = columns 64..127 = elements 16..31; dword 0 = elements 16..23 with
+    # codes 0..7, element k at nibble [0,1,4,5,2,3,6,7][k]: nibbles 0..7 hold
+    # 0,1,4,5,2,3,6,7 -> 0x76325410
+    assert u32_at(blob, 16 * 8) == 0x76325410
+    # lane 0 offsets: element m = 4t + e has offset t and sits at bit
+    # 16*(t%2) + ([0,4,10,14] if t < 2 else [2,6,8,12])[e]:
+    # t=1 -> 1 at bits 16,20,26,30 = 0x44110000; t=2 -> 2 at bits 2,6,8,12 =
+    # 0x00002288; t=3 -> 3 at bits 18,22,24,28 = 0x33CC0000
+    assert u32_at(blob, 512) == 0x77DD2288
+    assert u32_at(blob, 1024) == 0x48003C00
+    assert np.frombuffer(blob[768: 832].tobytes(), "<i4").tolist() == [0] + [-1] * 15
 
 
-def test_row_order_and_tiles():
+def test_row_order_and_mixed_class_record():
     gs = np.array([128, 32, 128, 32, 64, 128, 32], dtype=np.int32)
     assert layout.row_order(gs).tolist() == [1, 3, 6, 4, 0, 2, 5]
-    assert layout.tile_list(gs, 2) == [(0, 2, 32), (2, 1, 32), (3, 1, 64), (4, 2, 128), (6, 1, 128)]
+    N, K = 7, 256
+    gptr = np.concatenate([[0], np.cumsum(K // gs)]).astype(np.int32)
+    ng = int(gptr[-1])
+    assert ng == 3 * 8 + 4 + 3 * 2
+    kpr = K * 2 // 4
+    vals, offs = pack.pack_bytes(np.zeros((N, kpr), np.uint8), np.zeros((N, kpr), np.uint8))
+    canon = {"N": N, "K": K, "nk": 2, "group_size": gs, "vals": vals, "offs": offs,
+             "scale": np.arange(ng, dtype=np.uint16), "zero": np.zeros(ng, np.uint16), "gptr": gptr}
+    L = layout.build(canon)
+    # one record: rows in sorted order 1, 3, 6 (8 words each), 4 (4), 0, 2, 5 (2 each)
+    want = (list(range(gptr[1], gptr[2])) + list(range(gptr[3], gptr[4])) + list(range(gptr[6], gptr[7]))
+            + list(range(gptr[4], gptr[5])) + list(range(gptr[0], gptr[1])) + list(range(gptr[2], gptr[3]))
+            + list(range(gptr[5], gptr[6])))
+    assert L["sz"].tolist() == want
 
 
-@pytest.mark.parametrize("N,K,nk,RT,TPR", [
-    (7, 256, 2, 4, 4), (9, 768, 2, 2, 8), (11, 768, 1, 4, 4), (5, 1024, 1, 16, 16),
-    (13, 2816, 2, 4, 16), (6, 2816, 1, 8, 32), (3, 512, 2, 1, 64),
+def test_records_follow_chunks_within_a_block():
+    # K = 512: two chunks; a g32 row has 8 words per chunk, in chunk order
+    gs = np.array([32, 128], dtype=np.int32)
+    canon, _, _ = synthetic_canon(2, 512, 2, gs, seed=3)
+    L = layout.build(canon)
+    sz = canon["scale"].astype(np.uint32) | (canon["zero"].astype(np.uint32) << 16)
+    row0, row1 = sz[0:16], sz[16:20]
+    want = np.concatenate([row0[0:8], row1[0:2], row0[8:16], row1[2:4]])
+    assert np.array_equal(L["sz"], want)
+
+
+@pytest.mark.parametrize("N,K,nk", [
+    (7, 256, 2), (16, 512, 2), (17, 768, 2), (33, 512, 1), (5, 1024, 1), (40, 256, 1),
+    (3, 2816, 2), (19, 2816, 1),
 ])
-def test_decode_inverts_build(N, K, nk, RT, TPR):
+def test_decode_inverts_build(N, K, nk):
     rng = np.random.default_rng(N * K + nk)
-    choices = [g for g in (32, 64, 128, 256) if K % g == 0 and
-               (g <= 128 // nk or (TPR % (g // (128 // nk)) == 0 and (K * nk // 128) % (g // (128 // nk)) == 0))]
-    gs = rng.choice(choices, N).astype(np.int32)
+    gs = rng.choice([32, 64, 128, 256], N).astype(np.int32)
     canon, q, o = synthetic_canon(N, K, nk, gs, seed=N)
-    L = layout.build(canon, RT, TPR)
-    q2, o2, szr, perm = layout.decode(L["blob"], N, K, nk, RT, TPR)
+    L = layout.build(canon)
+    q2, o2, szr, perm = layout.decode(L["blob"], N, K, nk, gs)
     assert np.array_equal(q2, q) and np.array_equal(o2, o)
     sz = canon["scale"].astype(np.uint32) | (canon["zero"].astype(np.uint32) << 16)
     for n in range(N):
         assert np.array_equal(szr[n], sz[canon["gptr"][n]: canon["gptr"][n + 1]])
     assert sorted(perm.tolist()) == list(range(N))
+    # no byte is duplicated: the sections hold exactly the canonical bits plus zero padding
+    off = L["offsets"]
+    T = -(-N // 16)
+    assert off["offs"] >= T * (K // 256) * 64 * 8 * nk
+
+
+def test_off14_positions_are_a_permutation():
+    pos = [layout.off14_bit(m) for m in range(16)]
+    assert sorted(pos) == list(range(0, 32, 2))

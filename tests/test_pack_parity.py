@@ -22,7 +22,7 @@ def oracle_groups(L, W):
     return ogroups.select_groups(W, mask, L.Xcal(synth.CALIB_T), synth.FRAC_FINE, synth.G_FINE, synth.G_COARSE)
 
 
-def check_layer(L, rt=0, tpr=0, check_layout=True):
+def check_layer(L, check_layout=True):
     W = L.W()
     gs_o = oracle_groups(L, W)
     if L.adaptive:
@@ -33,17 +33,17 @@ def check_layer(L, rt=0, tpr=0, check_layout=True):
     canon_c = sg.pack(W, L.nk, gs_o)
     for k in ("vals", "offs", "scale", "zero", "gptr", "rowptr"):
         assert np.array_equal(canon_c[k], canon_o[k]), (L.name, k)
-    d = sg.describe(L.N, L.K, L.nk, gs_o, rt, tpr)
+    d = sg.describe(L.N, L.K, L.nk, gs_o)
     sz = opack.sizes(L.N, L.K, L.nk, gs_o)
     assert (d.kept, d.vals_bytes, d.offs_bytes, d.n_groups) == \
         (sz["kept"], sz["vals_bytes"], sz["offs_bytes"], sz["n_groups"])
     if check_layout:
         blob_c = sg.layout(d, canon_c)
-        lay = olayout.build(canon_o, d.rt, d.tpr)
+        lay = olayout.build(canon_o)
         off = lay["offsets"]
-        assert (d.off_perm, d.off_vals, d.off_offs, d.off_sz, d.blob_bytes) == \
-            (off["perm"], off["vals"], off["offs"], off["sz"], off["blob_bytes"])
-        assert d.n_tiles == len(lay["tiles"])
+        assert (d.off_codes, d.off_offs, d.off_perm, d.off_sz, d.blob_bytes) == \
+            (off["codes"], off["offs"], off["perm"], off["sz"], off["blob_bytes"])
+        assert d.n_blocks == -(-L.N // 16) and d.chunks == L.K // 256
         assert np.array_equal(blob_c, lay["blob"]), L.name
     return d
 
@@ -66,12 +66,17 @@ def test_decoder_set_sampled_layers():
         check_layer(L)
 
 
-@pytest.mark.parametrize("rt,tpr", [(64, 4), (32, 8), (16, 16), (8, 32), (4, 64), (2, 32), (1, 64)])
-def test_layout_parameters(rt, tpr):
-    L = synth.Layer("lay", 768, 200, 2, True, 9, 0, 0, 9)
-    check_layer(L, rt, tpr)
-    L1 = synth.Layer("lay1", 1280, 77, 1, True, 9, 1, 0, 9)
-    check_layer(L1, rt, tpr)
+@pytest.mark.parametrize("N,K,nk", [(200, 768, 2), (77, 1280, 1), (1, 256, 2), (15, 512, 1), (33, 11008, 2)])
+def test_ragged_blocks_and_mixed_classes(N, K, nk):
+    """Partial last row block, row blocks that straddle two group sizes, every size."""
+    rng = np.random.default_rng(N + K)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    gs = rng.choice([32, 64, 128, 256], N).astype(np.int32)
+    canon_o = opack.pack_canonical(W, nk, gs)
+    canon_c = sg.pack(W, nk, gs)
+    d = sg.describe(N, K, nk, gs)
+    assert list(d.class_rows) == [int(np.sum(gs == g)) for g in (32, 64, 128, 256)]
+    assert np.array_equal(sg.layout(d, canon_c), olayout.build(canon_o)["blob"])
 
 
 def test_quantizer_edge_groups():
@@ -129,10 +134,10 @@ def test_error_paths():
     with pytest.raises(sg.SgemvError):
         sg.describe(8, 256, 2, np.full(8, 48, np.int32))
     with pytest.raises(sg.SgemvError) as e:
-        sg.describe(8, 256, 2, g, rt=4, tpr=3)
+        sg.describe(8, 32768 + 256, 2, g)                      # K beyond 128 column chunks
     assert e.value.code == sg.sgemv.SGEMV_ESIZE
     with pytest.raises(sg.SgemvError) as e:
-        sg.describe(8, 11008, 2, np.full(8, 128, np.int32)[:8] * 0 + 64, rt=64, tpr=4)   # 43 chunks/thread
+        sg.describe(1 << 20, 32768, 2, np.full(1 << 20, 128, np.int32))   # blob of 2^31 bytes or more
     assert e.value.code == sg.sgemv.SGEMV_ESIZE
     W = np.zeros((8, 256), dtype=np.float16)
     W[3, 7] = np.nan
@@ -163,32 +168,68 @@ def test_error_paths():
 
 
 @pytest.mark.parametrize("seed", range(4))
-def test_launch_plan_covers_each_tile_once(seed):
-    """sgemv_plan (host arithmetic only): one workgroup per tile at batch 1, whole passes of
-    256 lanes per tile for beam batches; the LDS holds every staged x column of a phase."""
+def test_launch_plan_covers_every_chunk_once(seed):
+    """sgemv_plan (host arithmetic only): one workgroup per row block; its waves
+    split the column chunks in whole slices; x phases fit the 8 loads per lane
+    and the LDS holds every wave's slice plus the partial sums."""
     rng = np.random.default_rng(seed)
-    for _ in range(25):
+    for _ in range(40):
         nk = int(rng.choice([1, 2]))
-        K = int(rng.choice([256, 512, 768, 1024, 1280, 2816, 4096, 11008]))
-        N = int(rng.integers(1, 700))
-        gs = rng.choice([g for g in (32, 64, 128) if K % g == 0], N).astype(np.int32)
-        C = K * nk // 128
-        tpr = int(rng.choice([4, 8, 16, 32, 64]))
-        rt = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128, 256])) if seed else 0
-        try:
-            d = sg.describe(N, K, nk, gs, rt, tpr if rt else 0)
-        except sg.SgemvError:
-            continue
-        cpc = 128 // nk
-        for B in (1, 3, 16):
+        K = 256 * int(rng.choice([1, 2, 3, 4, 5, 11, 16, 43, 64, 65, 128]))
+        N = int(rng.integers(1, 12000))
+        gs = rng.choice([32, 64, 128, 256], N).astype(np.int32)
+        d = sg.describe(N, K, nk, gs)
+        C = K // 256
+        for B in (1, 2, 3, 4, 7, 8, 9, 16):
             pl = sg.plan(d, B)
-            slots = d.rt * d.tpr
-            if B == 1:
-                assert pl.grid == d.n_tiles and pl.pass_log2 == 0 and not pl.batched
-                assert pl.block * pl.rows_per_lane == slots and pl.block <= 256
-                assert pl.lds_bytes >= C * (cpc // 8 + 1) * 16          # all of x, with pads
-            else:
-                assert pl.batched and pl.grid == d.n_tiles << pl.pass_log2
-                assert pl.block << pl.pass_log2 == slots and pl.block <= 256
+            assert pl.grid == d.n_blocks == -(-N // 16)
+            assert pl.block == 64 * pl.waves and 1 <= pl.waves <= 16
+            assert 1 <= pl.chunks_per_wave <= 8
+            assert (pl.waves - 1) * pl.chunks_per_wave < C <= pl.waves * pl.chunks_per_wave
+            assert 1 <= pl.phase_chunks <= pl.chunks_per_wave
+            assert pl.x_loads == -(-(B * pl.phase_chunks * 32) // 64) and pl.x_loads <= 8
+            assert pl.lds_bytes == pl.waves * B * pl.phase_chunks * 512 + B * 16 * 16 * 4
             assert pl.lds_bytes <= 160 * 1024
-            assert pl.chunks_per_row_lane == -(-C // d.tpr)
+            assert pl.reserved == 0
+
+
+def test_plan_rejects_bad_batch_and_descriptor():
+    g = np.full(40, 64, np.int32)
+    d = sg.describe(40, 1024, 1, g)
+    for B in (0, 17, -1):
+        with pytest.raises(sg.SgemvError) as e:
+            sg.plan(d, B)
+        assert e.value.code == sg.sgemv.SGEMV_EINVAL
+    for field, delta in [("n_blocks", 1), ("chunks", -1), ("n_groups", 1), ("off_perm", 256), ("reserved", 1),
+                         ("blob_bytes", 256)]:
+        bad = sg.Desc.from_buffer_copy(d)
+        setattr(bad, field, getattr(bad, field) + delta)
+        with pytest.raises(sg.SgemvError) as e:
+            sg.plan(bad, 1)
+        assert e.value.code == sg.sgemv.SGEMV_ESIZE, field
+    bad = sg.Desc.from_buffer_copy(d)
+    bad.class_rows[0] += 1
+    bad.class_rows[1] -= 1
+    with pytest.raises(sg.SgemvError):
+        sg.plan(bad, 1)
+
+
+def test_layout_rejects_dequantised_weights_beyond_fp16():
+    """The kernel holds (code - zero) * scale in FP16: a group spanning [0, 65504]
+    gets scale fp16(65504/15) = 4368 and code 15 -> 65520, which rounds to +inf."""
+    N, K = 2, 256
+    W = np.zeros((N, K), np.float16)
+    W[1, 0] = 65504.0                     # row 1, group 0: lo = 0, hi = 65504
+    gs = np.full(N, 32, np.int32)
+    canon_o = opack.pack_canonical(W, 2, gs)
+    from oracle import gemv as ogemv
+    Wd = ogemv.dequant_dense(canon_o)
+    assert Wd[1, 0] == 65520.0 and np.isinf(np.float16(Wd[1, 0]))
+    canon_c = sg.pack(W, 2, gs)
+    d = sg.describe(N, K, 2, gs)
+    with pytest.raises(sg.SgemvError) as e:
+        sg.layout(d, canon_c)
+    assert e.value.code == sg.sgemv.SGEMV_EINVAL
+    W[1, 0] = 65000.0                     # scale 4332, 15 * 4332 = 64980: finite
+    canon_c = sg.pack(W, 2, gs)
+    assert sg.layout(d, canon_c).nbytes == d.blob_bytes
