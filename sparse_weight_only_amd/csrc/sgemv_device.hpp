@@ -102,14 +102,17 @@ __device__ __forceinline__ f4 smfmac(h8 a, h16 b, f4 c, uint32_t idx) {
   return __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, b, c, (int)idx, 0, ABID);
 }
 
-// Per-lane constants of one scale|zero word: (s, s), -(1024 + z), -(64 + z).
-struct Deq { h2 s, c1, c16; };
+// Per-lane constants of one scale|zero word: (s, s), (s, 0), (0, s),
+// -(1024 + z), -(64 + z).
+struct Deq { h2 s, s_lo, s_hi, c1, c16; };
 __device__ __forceinline__ Deq deq_consts(uint32_t szw) {
   const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
   const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)(szw >> 16));
   const _Float16 a = (_Float16)-1024.0f - z, b = (_Float16)-64.0f - z;   // exact: integers <= 1039
   Deq d;
   d.s = h2{s, s};
+  d.s_lo = h2{s, (_Float16)0.0f};
+  d.s_hi = h2{(_Float16)0.0f, s};
   d.c1 = h2{a, a};
   d.c16 = h2{b, b};
   return d;
@@ -234,6 +237,7 @@ __global__ __launch_bounds__(1024) void sgemv_kernel(KParams p) {
     const Deq d1 = deq_consts(g32 ? sv[i].y : sv[i].x);
     uint32_t idx2 = 0;
     if constexpr (NK == 1) idx2 = ((ov[i] & 0x33333333u) << 2) | ((ov[i] >> 2) & 0x33333333u);
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const Deq& d = t < 2 ? d0 : d1;
@@ -248,13 +252,15 @@ __global__ __launch_bounds__(1024) void sgemv_kernel(KParams p) {
         idx = ov[i][t >> 1];
       } else {
         // step t: 4 kept elements (one per group) in slots 0, 2, 5, 7; the
-        // other slot of each group holds 0
+        // other slot of each group holds 0: the scale pair (s, 0) or (0, s)
+        // keeps one half of the exact (q - z) pair
         const uint32_t cw = (t & 1) ? (cv[i][t >> 1] >> 8) : cv[i][t >> 1];
-        const uint32_t v02 = deq_lo(cw, magic, d), v13 = deq_hi(cw, magic, d);
-        a0 = v02 & 0x0000FFFFu;
-        a2 = v02 & 0xFFFF0000u;
-        a1 = v13 & 0x0000FFFFu;
-        a3 = v13 & 0xFFFF0000u;
+        const h2 q02 = as_h2((cw & 0x000F000Fu) | magic) + d.c1;
+        const h2 q13 = __builtin_elementwise_fma(as_h2((cw & 0x00F000F0u) | magic), sixteenth, d.c16);
+        a0 = as_u32(q02 * d.s_lo);
+        a2 = as_u32(q02 * d.s_hi);
+        a1 = as_u32(q13 * d.s_lo);
+        a3 = as_u32(q13 * d.s_hi);
         idx = t < 2 ? ov[i] : idx2;
       }
       const h2 A0 = as_h2(a0), A1 = as_h2(a1), A2 = as_h2(a2), A3 = as_h2(a3);

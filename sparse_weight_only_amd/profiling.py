@@ -2,7 +2,7 @@
 
 Usage (after the rocprofv3 runs named in each summary's header):
 
-    python -m sparse_weight_only_amd.profiling stats  <kernel_stats.csv> <out.txt> "<command>"
+    python -m sparse_weight_only_amd.profiling stats  <kernel_stats.csv> <out.txt> "<command>" [<kernel_trace.csv>]
     python -m sparse_weight_only_amd.profiling traffic <fetch counter_collection.csv>
                      <write counter_collection.csv> <out.json> "<fetch command>" "<write command>"
 
@@ -37,7 +37,7 @@ def short_name(name: str) -> str:
     return name.replace("(anonymous namespace)::", "").replace("sgemv_dev::", "").split("(")[0]
 
 
-def stats_summary(stats_csv: str, out_txt: str, command: str) -> None:
+def stats_summary(stats_csv: str, out_txt: str, command: str, trace_csv: str = None) -> None:
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [f"# rocprofv3 kernel statistics (kernel sources {kernel_source_hash()})",
              f"# command: {command}", "",
@@ -45,6 +45,22 @@ def stats_summary(stats_csv: str, out_txt: str, command: str) -> None:
     for r in rows:
         lines.append(f"{short_name(r['Name'])[:62]:62s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.3f} "
                      f"{float(r['MinNs']) / 1e3:9.3f} {float(r['MaxNs']) / 1e3:9.3f} {float(r['Percentage']):6.2f}")
+    if trace_csv:
+        # one kernel instantiation serves several layers: split its dispatches
+        # by launch shape (grid lanes x workgroup lanes), which names the layer
+        by = defaultdict(list)
+        for r in csv.DictReader(open(trace_csv)):
+            key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            by[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines += ["", "per launch shape (dispatch durations from the kernel trace, us)",
+                  f"{'kernel':40s} {'grid':>7s} {'wg':>5s} {'calls':>6s} {'avg':>7s} {'median':>7s} "
+                  f"{'p10':>7s} {'p90':>7s}"]
+        for (name, grid, wg), v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+            if len(v) < 20:
+                continue
+            q = statistics.quantiles(v, n=10)
+            lines.append(f"{name[:40]:40s} {grid:7d} {wg:5d} {len(v):6d} {statistics.mean(v):7.3f} "
+                         f"{statistics.median(v):7.3f} {q[0]:7.3f} {q[-1]:7.3f}")
     with open(out_txt, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -109,7 +125,7 @@ def _bench_layer_kernels() -> dict:
 
 if __name__ == "__main__":
     if len(sys.argv) >= 5 and sys.argv[1] == "stats":
-        stats_summary(sys.argv[2], sys.argv[3], sys.argv[4])
+        stats_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5] if len(sys.argv) > 5 else None)
     elif len(sys.argv) >= 7 and sys.argv[1] == "traffic":
         print(json.dumps(traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6],
                                          _bench_layer_kernels()), indent=1))
