@@ -20,6 +20,20 @@ Timing protocol
 * the oracle (NumPy FP64 dequantise-then-dot) is timed on the host cores on
   one pass over the same four layers.
 
+Beside the step, the same line reports
+* ``beam``: µs and GB/s per call of the beam-batch shapes (up and down of
+  decoder layers 0 (2:4) and 4 (1:4)) at B = 4, 8, 16, timed like the
+  per-layer figures;
+* ``decoder``: the 224 GEMVs of a 32-layer 7B-shaped decoder (q, k, v, o
+  4096 -> 4096, gate and up 4096 -> 11008, down 11008 -> 4096; 2:4 in the
+  first and last 4 layers, 1:4 elsewhere), launched back to back on one
+  stream, each with its own x and y; 20 replays of a graph of the whole
+  sequence. Every GEMV has its own device copy of its weights (1.79 GB in
+  all, so the sequence is cold by construction); the copies of one (shape,
+  N:M) pair are filled from one packed matrix, since the kernel's work and
+  bytes depend only on the shape, the N:M choice and the number of rows per
+  group size, which the adaptive policy fixes at ceil(N/10) fine rows.
+
 Prints one JSON line. ``--gpus N`` with N > 1 is refused: this build runs on
 one GPU.
 """
@@ -47,6 +61,8 @@ def parse():
     ap.add_argument("--layer-calls", type=int, default=400, help="launches per per-layer timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
+    ap.add_argument("--no-beam", action="store_true", help="skip the beam-batch figures")
+    ap.add_argument("--no-decoder", action="store_true", help="skip the 224-GEMV decoder sequence")
     return ap.parse_args()
 
 
@@ -230,6 +246,79 @@ def main():
                 "frac": round(d["GBps"] / HBM_PEAK_GBS, 4), "traffic": read_traffic(khash, dom),
                 "kernel": dom, "bytes_per_launch": d["bytes"], "us_per_launch": d["us_per_call"]}
 
+    def per_call_us(desc, copies, x, y, B, n_calls):
+        n_copies = len(copies)
+        n = n_copies * max(1, n_calls // (n_copies * 4))
+
+        def body():
+            cur = torch.cuda.current_stream(dev)
+            for i in range(n):
+                sg.run(desc, copies[i % n_copies].data_ptr(), x.data_ptr(), y.data_ptr(), B, cur.cuda_stream)
+
+        return timed(body, n, 4, 1) * 1e3
+
+    # ---- beam batches: up/down of decoder layers 0 (2:4) and 4 (1:4), B = 4, 8, 16
+    beam = None
+    if not args.no_beam:
+        beam = {}
+        for L in synth.cfg5():
+            W = L.W()
+            gs = sg.select_groups(W, L.nk, L.Xcal(synth.CALIB_T), synth.FRAC_FINE, synth.G_FINE, synth.G_COARSE)
+            desc = sg.describe(L.N, L.K, L.nk, gs)
+            host = torch.from_numpy(sg.layout(desc, sg.pack(W, L.nk, gs)))
+            R = max(2, -(-COLD_BYTES // desc.blob_bytes))
+            copies = [host.to(dev) for _ in range(R)]
+            beam[L.name] = {}
+            for B in synth.CFG5_BATCHES:
+                x = torch.from_numpy(L.X(B)).to(dev)
+                y = torch.empty((B, L.N), dtype=torch.float16, device=dev)
+                us = per_call_us(desc, copies, x, y, B, args.layer_calls)
+                nb = sg.algorithmic_bytes(desc, B)
+                beam[L.name][str(B)] = {"us_per_call": round(us, 3), "bytes": nb,
+                                        "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                                        "pct_hbm_peak": round(100 * nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+            del copies
+            torch.cuda.empty_cache()
+        log("beam batches timed")
+
+    # ---- 224-GEMV decoder sequence, one launch per GEMV
+    decoder = None
+    if not args.no_decoder:
+        reps_dec = 20
+        packed = {}
+        for l in (0, 4):                        # one packed matrix per (shape, N:M)
+            for m, (name, K, N) in enumerate(synth.LLAMA7B_MATS):
+                key = (K, N, synth.layer_nk(l))
+                if key in packed:
+                    continue
+                L = synth.Layer(f"decoder_l{l:02d}_{name}", K, N, key[2], True, 4, l, m, 4)
+                W = L.W()
+                gs = sg.select_groups(W, L.nk, L.Xcal(synth.CALIB_T), synth.FRAC_FINE, synth.G_FINE, synth.G_COARSE)
+                desc = sg.describe(N, K, L.nk, gs)
+                packed[key] = (desc, torch.from_numpy(sg.layout(desc, sg.pack(W, L.nk, gs))))
+        seq = []
+        dec_bytes = 0
+        for i, L in enumerate(synth.cfg4()):
+            desc, host = packed[(L.K, L.N, L.nk)]
+            seq.append((desc, host.to(dev), torch.from_numpy(L.X(1)).to(dev),
+                        torch.empty((1, L.N), dtype=torch.float16, device=dev)))
+            dec_bytes += sg.algorithmic_bytes(desc, 1)
+        torch.cuda.synchronize()
+
+        def body_decoder():
+            cur = torch.cuda.current_stream(dev)
+            for (desc, blob, x, y) in seq:
+                sg.run(desc, blob.data_ptr(), x.data_ptr(), y.data_ptr(), 1, cur.cuda_stream)
+
+        ms_seq = timed(body_decoder, 1, reps_dec, 2)
+        decoder = {"gemvs": len(seq), "launches": len(seq), "us_per_sequence": round(ms_seq * 1e3, 2),
+                   "bytes": dec_bytes, "GBps": round(dec_bytes / (ms_seq * 1e-3) / 1e9, 1),
+                   "pct_hbm_peak": round(100 * dec_bytes / (ms_seq * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                   "replays": reps_dec}
+        del seq, packed
+        torch.cuda.empty_cache()
+        log("decoder sequence timed")
+
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": warm * S, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
@@ -245,6 +334,10 @@ def main():
         "kernel_source_hash": khash,
         "pack_seconds": round(t_pack, 2),
     }
+    if beam is not None:
+        out["beam"] = beam
+    if decoder is not None:
+        out["decoder"] = decoder
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers_host)
     print(json.dumps(out), flush=True)

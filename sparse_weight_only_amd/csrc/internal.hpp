@@ -76,7 +76,11 @@ inline int piece_offs_bytes(int nk) { return 4 * nk; }    // 2 bits per kept ele
 struct Launch { int waves, cpw, imax, phase, xloads, xmax; int64_t lds; };
 inline Launch launch_geometry(int C, int T, int B) {
   Launch L;
-  int cpw = 4;
+  // up to 4 vectors, two chunks per wave where that keeps the workgroup
+  // within 16 waves: a wave with fewer loads to issue starts computing
+  // sooner, which hides more of the dequantisation under the data phase.
+  // Otherwise (and for larger batches, whose x slices dominate) four.
+  int cpw = (B <= 4 && (C + 1) / 2 <= kMaxWaves) ? 2 : 4;
   // smaller slices when the layer has few row blocks, so the grid has
   // enough waves to cover the chip (256 CUs x 4 SIMDs, two waves each)
   while (cpw > 1 && (int64_t)T * ((C + cpw - 1) / cpw) < 2048) cpw /= 2;
