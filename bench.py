@@ -28,7 +28,9 @@ Beside the step, the same line reports
   4096 -> 4096, gate and up 4096 -> 11008, down 11008 -> 4096; 2:4 in the
   first and last 4 layers, 1:4 elsewhere), launched back to back on one
   stream, each with its own x and y; 20 replays of a graph of the whole
-  sequence. Every GEMV has its own device copy of its weights (1.79 GB in
+  sequence, once with one launch per GEMV and once with the launches a
+  decode step can group (q, k and v together; o; gate and up together;
+  down: 4 launches per layer, sgemv_run_group). Every GEMV has its own device copy of its weights (1.79 GB in
   all, so the sequence is cold by construction); the copies of one (shape,
   N:M) pair are filled from one packed matrix, since the kernel's work and
   bytes depend only on the shape, the N:M choice and the number of rows per
@@ -310,11 +312,29 @@ def main():
             for (desc, blob, x, y) in seq:
                 sg.run(desc, blob.data_ptr(), x.data_ptr(), y.data_ptr(), 1, cur.cuda_stream)
 
+        # the same GEMVs grouped as a decode step can issue them: q, k, v
+        # (inputs ready together); o; gate, up; down -> 4 launches per layer
+        names = [name for name, _, _ in synth.LLAMA7B_MATS]
+        launch_groups = [["q_proj", "k_proj", "v_proj"], ["o_proj"], ["gate_proj", "up_proj"], ["down_proj"]]
+        grouped = []
+        for l0 in range(0, len(seq), len(names)):
+            for grp in launch_groups:
+                grouped.append([(seq[l0 + names.index(m)][0], seq[l0 + names.index(m)][1].data_ptr(),
+                                 seq[l0 + names.index(m)][2].data_ptr(), seq[l0 + names.index(m)][3].data_ptr())
+                                for m in grp])
+
+        def body_grouped():
+            cur = torch.cuda.current_stream(dev)
+            for tasks in grouped:
+                sg.run_group(tasks, 1, cur.cuda_stream)
+
         ms_seq = timed(body_decoder, 1, reps_dec, 2)
-        decoder = {"gemvs": len(seq), "launches": len(seq), "us_per_sequence": round(ms_seq * 1e3, 2),
-                   "bytes": dec_bytes, "GBps": round(dec_bytes / (ms_seq * 1e-3) / 1e9, 1),
-                   "pct_hbm_peak": round(100 * dec_bytes / (ms_seq * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-                   "replays": reps_dec}
+        ms_grp = timed(body_grouped, 1, reps_dec, 2)
+        rate = lambda ms: {"us_per_sequence": round(ms * 1e3, 2), "GBps": round(dec_bytes / (ms * 1e-3) / 1e9, 1),
+                           "pct_hbm_peak": round(100 * dec_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+        decoder = {"gemvs": len(seq), "bytes": dec_bytes, "replays": reps_dec,
+                   "one_launch_per_gemv": dict(launches=len(seq), **rate(ms_seq)),
+                   "grouped_qkv_o_gateup_down": dict(launches=len(grouped), **rate(ms_grp))}
         del seq, packed
         torch.cuda.empty_cache()
         log("decoder sequence timed")

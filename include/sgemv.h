@@ -170,6 +170,43 @@ typedef struct sgemv_plan_t {
  * Errors: EINVAL (NULL, B outside 1..16), ESIZE (inconsistent descriptor). */
 int sgemv_plan(const sgemv_desc* d, int32_t B, sgemv_plan_t* out);
 
+/* One layer of a several-layer launch (sgemv_run_group): the arguments of
+ * sgemv_run for that layer. */
+typedef struct sgemv_task {
+  const sgemv_desc* desc;  /* host pointer to the layer's descriptor          */
+  const void* blob_dev;    /* device blob, 256-byte aligned                   */
+  const void* x_dev;       /* device FP16 [B][desc->K], 16-byte aligned       */
+  void* y_dev;             /* device FP16 [B][desc->N], 2-byte aligned        */
+} sgemv_task;
+
+#define SGEMV_MAX_GROUP 32
+
+/* sgemv_run_group - several independent GEMVs y_i = W'_i x_i in one kernel
+ * launch (the per-token decode of P1 §1 runs many small GEMVs back to back;
+ * one launch per GEMV pays the dispatch, ramp-up and drain of a kernel each
+ * time, which a 4096 x 4096 layer's few megabytes cannot hide).
+ *   tasks      : host array of count layers; every layer has the same nk
+ *                (EINVAL otherwise); N and K may differ (workgroups of a
+ *                layer with fewer column chunks than the widest one leave
+ *                waves idle, so grouping layers of equal K is best).
+ *   count      : 1..SGEMV_MAX_GROUP.
+ *   B          : batch of every layer, 1..16.
+ *   hip_stream : hipStream_t to enqueue on (NULL = default stream).
+ * Results are those of sgemv_run on each layer, with the same bound; the sum
+ * over column chunks may be split differently (the launch geometry follows
+ * the widest layer and the summed row blocks, see sgemv_plan_group), so the
+ * bits can differ from separate calls by FP32 reassociation. Outputs must
+ * not overlap each other, any x or any blob. Enqueues one kernel and
+ * returns without synchronising.
+ * Errors: EINVAL (count, B, NULL, mixed nk), ESIZE (inconsistent descriptor
+ * or sizes beyond the kernels), EALIGN, EHIP. */
+int sgemv_run_group(const sgemv_task* tasks, int32_t count, int32_t B, void* hip_stream);
+
+/* sgemv_plan_group - the launch sgemv_run_group would make (grid = summed
+ * row blocks), without any HIP call. Device pointers are not examined.
+ * Errors: as sgemv_run_group except EALIGN and EHIP. */
+int sgemv_plan_group(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_plan_t* out);
+
 /* sgemv_strerror - static description of a status code (never NULL). */
 const char* sgemv_strerror(int code);
 

@@ -143,11 +143,10 @@ __device__ __forceinline__ int words_before(const KParams& p, int i) {
   return s;
 }
 
+// Row block rb of the layer p, computed by the whole workgroup.
 template <int NK, int IMAX, int XMAX>
-__global__ __launch_bounds__(1024) void sgemv_kernel(KParams p) {
+__device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int rb = blockIdx.x;
-  if (rb >= p.T) return;
   constexpr int CB = 8 * NK, OB = 4 * NK;   // bytes of one piece's codes and offsets
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, W = blockDim.x >> 6;
   const int r = lane & 15, q = lane >> 4;
@@ -298,6 +297,34 @@ __global__ __launch_bounds__(1024) void sgemv_kernel(KParams p) {
     const int n = (int)orow;
     if (n >= 0 && n < p.N) p.y[(int64_t)b * p.N + n] = __builtin_bit_cast(uint16_t, (_Float16)s);
   }
+}
+
+// One launch, one layer: workgroup b computes row block b.
+template <int NK, int IMAX, int XMAX>
+__global__ __launch_bounds__(1024) void sgemv_kernel(KParams p) {
+  if ((int)blockIdx.x >= p.T) return;
+  sgemv_block<NK, IMAX, XMAX>(p, (int)blockIdx.x);
+}
+
+// One launch, several independent layers with the same N:M choice, batch and
+// chunks per wave: workgroup b computes row block b - first_block[i] of layer
+// i, the layer whose block range holds b. Layers with fewer chunks than the
+// workgroup's waves cover leave the extra waves idle (they add zeros).
+constexpr int kMaxGroup = 32;
+struct GParams {
+  int32_t count;
+  int32_t first_block[kMaxGroup + 1];
+  KParams t[kMaxGroup];
+};
+static_assert(sizeof(GParams) <= 4096, "kernel arguments are limited to 4 KiB");
+
+template <int NK, int IMAX, int XMAX>
+__global__ __launch_bounds__(1024) void sgemv_group_kernel(GParams g) {
+  const int b = (int)blockIdx.x;
+  if (b >= g.first_block[g.count]) return;
+  int i = 0;
+  while (i + 1 < g.count && b >= g.first_block[i + 1]) ++i;
+  sgemv_block<NK, IMAX, XMAX>(g.t[i], b - g.first_block[i]);
 }
 
 }  // namespace sgemv_dev

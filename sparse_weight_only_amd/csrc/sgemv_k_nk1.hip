@@ -15,6 +15,16 @@ KernelFn by_xmax(int xmax) {
     default: return nullptr;
   }
 }
+template <int IMAX>
+GroupFn group_by_xmax(int xmax) {
+  switch (xmax) {
+    case 1: return sgemv_group_kernel<1, IMAX, 1>;
+    case 2: return sgemv_group_kernel<1, IMAX, 2>;
+    case 4: return sgemv_group_kernel<1, IMAX, 4>;
+    case 8: return sgemv_group_kernel<1, IMAX, 8>;
+    default: return nullptr;
+  }
+}
 }  // namespace
 
 KernelFn get_kernel_nk1(int imax, int xmax) {
@@ -23,6 +33,16 @@ KernelFn get_kernel_nk1(int imax, int xmax) {
     case 2: return by_xmax<2>(xmax);
     case 4: return by_xmax<4>(xmax);
     case 8: return by_xmax<8>(xmax);
+    default: return nullptr;
+  }
+}
+
+GroupFn get_group_kernel_nk1(int imax, int xmax) {
+  switch (imax) {
+    case 1: return group_by_xmax<1>(xmax);
+    case 2: return group_by_xmax<2>(xmax);
+    case 4: return group_by_xmax<4>(xmax);
+    case 8: return group_by_xmax<8>(xmax);
     default: return nullptr;
   }
 }

@@ -6,6 +6,10 @@
 #include "sgemv_device.hpp"
 
 using namespace sgemv;
+using sgemv_dev::GParams;
+using sgemv_dev::GroupFn;
+using sgemv_dev::kMaxGroup;
+static_assert(sgemv_dev::kMaxGroup == SGEMV_MAX_GROUP, "group size limit");
 using sgemv_dev::KernelFn;
 using sgemv_dev::KParams;
 
@@ -57,6 +61,63 @@ int make_plan(const sgemv_desc* d, int32_t B, sgemv_plan_t* pl, Launch* geo) {
   return SGEMV_OK;
 }
 
+// Kernel parameters of one layer under a launch geometry.
+KParams make_params(const sgemv_desc* d, const void* blob, const void* x, void* y, int32_t B, const Launch& L) {
+  KParams p;
+  p.blob = (const uint8_t*)blob;
+  p.x = (const uint16_t*)x;
+  p.y = (uint16_t*)y;
+  p.blob_bytes = (uint32_t)d->blob_bytes;
+  p.off_codes = (uint32_t)d->off_codes;
+  p.off_offs = (uint32_t)d->off_offs;
+  p.off_perm = (uint32_t)d->off_perm;
+  p.off_sz = (uint32_t)d->off_sz;
+  p.N = d->N; p.K = d->K; p.B = B; p.C = d->chunks;
+  p.cpw = L.cpw;
+  p.phase = L.phase;
+  p.T = d->n_blocks;
+  p.cls_row[0] = 0;
+  for (int c = 0; c < 4; ++c) p.cls_row[c + 1] = p.cls_row[c] + d->class_rows[c];
+  return p;
+}
+
+bool aligned(const void* blob, const void* x, const void* y) {
+  return !(((uintptr_t)blob % 256) || ((uintptr_t)x % 16) || ((uintptr_t)y % 2));
+}
+
+// What sgemv_run_group launches: one geometry for the widest layer and the
+// summed row blocks; pure host arithmetic.
+int make_group_plan(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_plan_t* pl, Launch* geo) {
+  if (!tasks || !pl) return SGEMV_EINVAL;
+  if (count < 1 || count > kMaxGroup || B < 1 || B > 16) return SGEMV_EINVAL;
+  int64_t blocks = 0;
+  int32_t cmax = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const sgemv_desc* d = tasks[i].desc;
+    if (!d) return SGEMV_EINVAL;
+    if (!desc_consistent(d)) return SGEMV_ESIZE;
+    if (d->nk != tasks[0].desc->nk) return SGEMV_EINVAL;
+    blocks += d->n_blocks;
+    cmax = d->chunks > cmax ? d->chunks : cmax;
+  }
+  if (blocks > ((int64_t)1 << 30)) return SGEMV_ESIZE;
+  const Launch L = launch_geometry(cmax, (int32_t)blocks, B);
+  if (L.waves < 1 || L.waves > kMaxWaves || L.cpw > kMaxChunksPerWave || L.xloads > 8) return SGEMV_ESIZE;
+  if (L.lds > 160 * 1024) return SGEMV_ESIZE;
+  sgemv_plan_t q;
+  memset(&q, 0, sizeof q);
+  q.grid = blocks;
+  q.lds_bytes = L.lds;
+  q.block = 64 * L.waves;
+  q.waves = L.waves;
+  q.chunks_per_wave = L.cpw;
+  q.phase_chunks = L.phase;
+  q.x_loads = L.xloads;
+  *pl = q;
+  if (geo) *geo = L;
+  return SGEMV_OK;
+}
+
 }  // namespace
 
 extern "C" int sgemv_plan(const sgemv_desc* d, int32_t B, sgemv_plan_t* out) {
@@ -70,22 +131,8 @@ extern "C" int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* 
   Launch L;
   const int rc = make_plan(d, B, &pl, &L);
   if (rc) return rc;
-  if (((uintptr_t)blob_dev % 256) || ((uintptr_t)x_dev % 16) || ((uintptr_t)y_dev % 2)) return SGEMV_EALIGN;
-  KParams p;
-  p.blob = (const uint8_t*)blob_dev;
-  p.x = (const uint16_t*)x_dev;
-  p.y = (uint16_t*)y_dev;
-  p.blob_bytes = (uint32_t)d->blob_bytes;
-  p.off_codes = (uint32_t)d->off_codes;
-  p.off_offs = (uint32_t)d->off_offs;
-  p.off_perm = (uint32_t)d->off_perm;
-  p.off_sz = (uint32_t)d->off_sz;
-  p.N = d->N; p.K = d->K; p.B = B; p.C = d->chunks;
-  p.cpw = L.cpw;
-  p.phase = L.phase;
-  p.T = d->n_blocks;
-  p.cls_row[0] = 0;
-  for (int c = 0; c < 4; ++c) p.cls_row[c + 1] = p.cls_row[c] + d->class_rows[c];
+  if (!aligned(blob_dev, x_dev, y_dev)) return SGEMV_EALIGN;
+  const KParams p = make_params(d, blob_dev, x_dev, y_dev, B, L);
   KernelFn fn = sgemv_dev::get_kernel(d->nk, L.imax, L.xmax);
   if (!fn) return SGEMV_ESIZE;
   if (pl.lds_bytes > 65536) {
@@ -93,6 +140,37 @@ extern "C" int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* 
       return SGEMV_EHIP;
   }
   hipLaunchKernelGGL(fn, dim3((uint32_t)pl.grid), dim3(pl.block), (uint32_t)pl.lds_bytes, (hipStream_t)hip_stream, p);
+  if (hipGetLastError() != hipSuccess) return SGEMV_EHIP;
+  return SGEMV_OK;
+}
+
+extern "C" int sgemv_plan_group(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_plan_t* out) {
+  return make_group_plan(tasks, count, B, out, nullptr);
+}
+
+extern "C" int sgemv_run_group(const sgemv_task* tasks, int32_t count, int32_t B, void* hip_stream) {
+  sgemv_plan_t pl;
+  Launch L;
+  const int rc = make_group_plan(tasks, count, B, &pl, &L);
+  if (rc) return rc;
+  GParams g;
+  memset(&g, 0, sizeof g);
+  g.count = count;
+  g.first_block[0] = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const sgemv_task& t = tasks[i];
+    if (!t.blob_dev || !t.x_dev || !t.y_dev) return SGEMV_EINVAL;
+    if (!aligned(t.blob_dev, t.x_dev, t.y_dev)) return SGEMV_EALIGN;
+    g.t[i] = make_params(t.desc, t.blob_dev, t.x_dev, t.y_dev, B, L);
+    g.first_block[i + 1] = g.first_block[i] + t.desc->n_blocks;
+  }
+  GroupFn fn = sgemv_dev::get_group_kernel(tasks[0].desc->nk, L.imax, L.xmax);
+  if (!fn) return SGEMV_ESIZE;
+  if (pl.lds_bytes > 65536) {
+    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds_bytes) != hipSuccess)
+      return SGEMV_EHIP;
+  }
+  hipLaunchKernelGGL(fn, dim3((uint32_t)pl.grid), dim3(pl.block), (uint32_t)pl.lds_bytes, (hipStream_t)hip_stream, g);
   if (hipGetLastError() != hipSuccess) return SGEMV_EHIP;
   return SGEMV_OK;
 }

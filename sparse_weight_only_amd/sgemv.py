@@ -57,6 +57,15 @@ class Plan(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class Task(ctypes.Structure):
+    """One layer of a several-layer launch (mirrors sgemv_task)."""
+    _fields_ = [("desc", ctypes.POINTER(Desc)), ("blob_dev", ctypes.c_void_p),
+                ("x_dev", ctypes.c_void_p), ("y_dev", ctypes.c_void_p)]
+
+
+MAX_GROUP = 32
+
+
 def lib_path() -> str:
     return _LIB_PATH
 
@@ -77,9 +86,12 @@ def lib():
         L.sgemv_layout.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P, P]
         L.sgemv_run.argtypes = [ctypes.POINTER(Desc), P, P, P, i32, P]
         L.sgemv_plan.argtypes = [ctypes.POINTER(Desc), i32, ctypes.POINTER(Plan)]
+        L.sgemv_run_group.argtypes = [ctypes.POINTER(Task), i32, i32, P]
+        L.sgemv_plan_group.argtypes = [ctypes.POINTER(Task), i32, i32, ctypes.POINTER(Plan)]
         L.sgemv_strerror.argtypes = [ctypes.c_int]
         L.sgemv_strerror.restype = ctypes.c_char_p
-        for f in ("sgemv_describe", "sgemv_select_groups", "sgemv_pack", "sgemv_layout", "sgemv_run", "sgemv_plan"):
+        for f in ("sgemv_describe", "sgemv_select_groups", "sgemv_pack", "sgemv_layout", "sgemv_run", "sgemv_plan",
+                  "sgemv_run_group", "sgemv_plan_group"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -168,6 +180,27 @@ def plan(desc: Desc, B: int) -> Plan:
     """The launch sgemv_run would make for (desc, B); no GPU needed."""
     pl = Plan()
     _check(lib().sgemv_plan(ctypes.byref(desc), B, ctypes.byref(pl)), "sgemv_plan")
+    return pl
+
+
+def _tasks(tasks):
+    """[(desc, blob_dev, x_dev, y_dev), ...] -> ctypes array of Task (descs kept alive by the caller)."""
+    arr = (Task * max(1, len(tasks)))()
+    for i, (d, blob, x, y) in enumerate(tasks):
+        arr[i] = Task(ctypes.pointer(d), ctypes.c_void_p(blob), ctypes.c_void_p(x), ctypes.c_void_p(y))
+    return arr
+
+
+def run_group(tasks, B: int, stream: int = 0) -> None:
+    """Enqueue several independent GEMVs (same N:M choice) as one launch;
+    ``tasks`` lists (desc, blob_dev, x_dev, y_dev) with raw device pointers."""
+    _check(lib().sgemv_run_group(_tasks(tasks), len(tasks), B, ctypes.c_void_p(stream)), "sgemv_run_group")
+
+
+def plan_group(tasks, B: int) -> Plan:
+    """The launch sgemv_run_group would make; no GPU needed (pointers may be 0)."""
+    pl = Plan()
+    _check(lib().sgemv_plan_group(_tasks(tasks), len(tasks), B, ctypes.byref(pl)), "sgemv_plan_group")
     return pl
 
 

@@ -177,3 +177,89 @@ def test_every_launch_geometry(nk, N, K):
         y_ref, D, _ = oracle_y(layer.canon, X)
         err = ogemv.normalized_error(y, y_ref, D)
         assert err <= TOL, (B, err)
+
+
+def _run_group_checked(layers, Xs, B, guard=64):
+    """One sgemv_run_group launch over layers (each with its own x and guarded y)."""
+    import torch
+    sentinel = np.uint16(0x7E5A)
+    bufs, tasks, xs = [], [], []
+    for layer, X in zip(layers, Xs):
+        N = layer.desc.N
+        x = torch.from_numpy(np.ascontiguousarray(X)).cuda()
+        ybuf = torch.full((B * N + 2 * guard,), int(np.int16(sentinel.view(np.int16))), dtype=torch.int16, device="cuda")
+        xs.append(x)
+        bufs.append(ybuf)
+        tasks.append((layer.desc, layer.blob.data_ptr(), x.data_ptr(), ybuf[guard:].data_ptr()))
+    sg.run_group(tasks, B, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    out = []
+    for layer, ybuf in zip(layers, bufs):
+        host = ybuf.cpu().numpy().view(np.uint16)
+        assert np.all(host[:guard] == sentinel) and np.all(host[-guard:] == sentinel), "y guard band overwritten"
+        out.append(host[guard: guard + B * layer.desc.N].reshape(B, layer.desc.N).view(np.float16))
+    return out
+
+
+@pytest.mark.parametrize("nk", [2, 1])
+def test_group_launch_exact_arithmetic(nk):
+    """Several layers of different N and K in one launch: bit-exact on grid weights."""
+    rng = np.random.default_rng(40 + nk)
+    shapes = [(600, 4096), (33, 4096), (1000, 2048), (77, 11008), (16, 256), (300, 4096)]
+    layers = []
+    for N, K in shapes:
+        gs = rng.choice([32, 64, 128, 256], N).astype(np.int32)
+        W = np.zeros((N, K), np.float16)
+        for g in np.unique(gs):
+            W[gs == g] = grid_weights(int((gs == g).sum()), K, nk, int(g), rng)
+        layers.append(make_layer(W, nk, gs))
+    for B in (1, 3, 16):
+        say(f"case group exact nk={nk} B={B} layers={shapes}")
+        Xs = []
+        for N, K in shapes:
+            X = np.zeros((B, K), np.float16)
+            for b in range(B):
+                idx = rng.choice(K, size=min(64, K), replace=False)
+                X[b, idx] = rng.choice([-1.0, 1.0], len(idx))
+            Xs.append(X)
+        ys = _run_group_checked(layers, Xs, B)
+        for layer, X, y in zip(layers, Xs, ys):
+            y_ref, D, _ = oracle_y(layer.canon, X)
+            want = y_ref.astype(np.float16)
+            assert np.array_equal(want.astype(np.float64), y_ref), "reference not exact"
+            assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), (layer.desc.N, layer.desc.K, B)
+
+
+def test_group_launch_many_small_layers():
+    """32 layers (the maximum) in one launch: every row block lands in its own layer."""
+    rng = np.random.default_rng(77)
+    layers, Xs = [], []
+    for i in range(32):
+        N, K = int(rng.integers(1, 70)), 256 * int(rng.integers(1, 6))
+        W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+        gs = rng.choice([32, 128], N).astype(np.int32)
+        layers.append(make_layer(W, 2, gs))
+        Xs.append(rng.standard_normal((2, K)).astype(np.float16))
+    say("case group of 32 small layers")
+    ys = _run_group_checked(layers, Xs, 2)
+    for layer, X, y in zip(layers, Xs, ys):
+        y_ref, D, _ = oracle_y(layer.canon, X)
+        assert ogemv.normalized_error(y, y_ref, D) <= TOL
+
+
+def test_group_launch_decoder_layer():
+    """The GEMVs of decoder layer 0 grouped as a decode step issues them (q, k, v; o; gate, up; down)."""
+    Ls = [L for L in synth.cfg4() if L.layer == 0]
+    made = {L.name: (L, make_layer(L.W(), L.nk, group_sizes(L, L.W()))) for L in Ls}
+    groups = [["q_proj", "k_proj", "v_proj"], ["o_proj"], ["gate_proj", "up_proj"], ["down_proj"]]
+    for grp in groups:
+        members = [made[f"cfg4_l00_{m}"] for m in grp]
+        say(f"case group decoder layer 0: {grp}")
+        ys = _run_group_checked([lay for _, lay in members], [L.X(1) for L, _ in members], 1)
+        for (L, layer), y in zip(members, ys):
+            y_ref, D, _ = oracle_y(layer.canon, L.X(1))
+            err = ogemv.normalized_error(y, y_ref, D)
+            assert err <= TOL, (L.name, err)
+            if len(grp) == 1:
+                # a group of one is the single call: same kernel, same geometry, same bits
+                assert np.array_equal(y.view(np.uint16), run_checked(layer, L.X(1)).view(np.uint16))

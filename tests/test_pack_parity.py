@@ -233,3 +233,51 @@ def test_layout_rejects_dequantised_weights_beyond_fp16():
     W[1, 0] = 65000.0                     # scale 4332, 15 * 4332 = 64980: finite
     canon_c = sg.pack(W, 2, gs)
     assert sg.layout(d, canon_c).nbytes == d.blob_bytes
+
+
+def test_group_plan_and_host_errors():
+    """sgemv_plan_group / sgemv_run_group host checks (no HIP call before them)."""
+    rng = np.random.default_rng(11)
+    E = sg.sgemv
+    shapes = [(4096, 4096), (4096, 4096), (11008, 4096), (4096, 11008), (17, 256)]
+    descs = {}
+    for nk in (1, 2):
+        descs[nk] = [sg.describe(N, K, nk, rng.choice([32, 128], N).astype(np.int32)) for N, K in shapes]
+    fake = lambda ds: [(d, 0x1000 * (i + 1), 0x100000, 0x200000 + 0x40000 * i) for i, d in enumerate(ds)]
+    for nk in (1, 2):
+        for B in (1, 4, 16):
+            for k in range(1, len(shapes) + 1):
+                ds = descs[nk][:k]
+                pl = sg.plan_group(fake(ds), B)
+                cmax = max(d.chunks for d in ds)
+                assert pl.grid == sum(d.n_blocks for d in ds)
+                assert pl.block == 64 * pl.waves and 1 <= pl.waves <= 16
+                assert (pl.waves - 1) * pl.chunks_per_wave < cmax <= pl.waves * pl.chunks_per_wave
+                assert pl.lds_bytes == pl.waves * B * pl.phase_chunks * 512 + B * 16 * 16 * 4
+            # a group of one is planned like the single call
+            for d in descs[nk]:
+                a, b = sg.plan_group(fake([d]), B), sg.plan(d, B)
+                assert a.as_dict() == b.as_dict()
+    # up to 32 layers; 0, 33 and mixed N:M choices are rejected
+    small = sg.describe(16, 256, 2, np.full(16, 128, np.int32))
+    assert sg.plan_group(fake([small] * 32), 1).grid == 32
+    for tasks, B, code in [([], 1, E.SGEMV_EINVAL), (fake([small] * 33), 1, E.SGEMV_EINVAL),
+                           (fake([descs[1][0], descs[2][0]]), 1, E.SGEMV_EINVAL),
+                           (fake([small]), 0, E.SGEMV_EINVAL), (fake([small]), 17, E.SGEMV_EINVAL)]:
+        with pytest.raises(sg.SgemvError) as e:
+            sg.plan_group(tasks, B)
+        assert e.value.code == code
+        with pytest.raises(sg.SgemvError) as e:
+            sg.run_group(tasks, B)
+        assert e.value.code == code
+    bad = sg.Desc.from_buffer_copy(small)
+    bad.n_blocks += 1
+    with pytest.raises(sg.SgemvError) as e:
+        sg.run_group(fake([small, bad]), 1)
+    assert e.value.code == E.SGEMV_ESIZE
+    for task, code in [((small, 0x1001, 0x1000, 0x1000), E.SGEMV_EALIGN), ((small, 0x1000, 0x1008, 0x1000), E.SGEMV_EALIGN),
+                       ((small, 0x1000, 0x1000, 0x1001), E.SGEMV_EALIGN), ((small, 0, 0x1000, 0x1000), E.SGEMV_EINVAL),
+                       ((small, 0x1000, 0x1000, 0), E.SGEMV_EINVAL)]:
+        with pytest.raises(sg.SgemvError) as e:
+            sg.run_group(fake([small]) + [task], 1)
+        assert e.value.code == code
