@@ -89,6 +89,23 @@ int sgemv_select_groups(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
                         const uint16_t* xcal, int32_t T, double frac_fine,
                         int32_t g_fine, int32_t g_coarse, int32_t* group_size_out);
 
+/* sgemv_prune - N:M pruning by the activation-aware importance of P1 §3.2
+ * (eq. (3), first term): score(n, k) = |w[n][k]| * c_k with
+ * c_k = sqrt(sum_t xcal[t][k]^2) (FP64, sequential over t). In every group of
+ * 4 consecutive columns of a row the nk largest scores are kept (ties: lower
+ * column); the gradient term of eq. (3) is not used (it needs a loss).
+ *   w      : host FP16 bits [N][K], dense weights.
+ *   xcal, T: host FP16 bits [T][K] calibration activations, T >= 1; NULL for
+ *            unit column scales (score |w|, the selection sgemv_pack makes).
+ *   w_out  : host FP16 bits [N][K]: the kept values, bits unchanged, and +0
+ *            at pruned positions (may not alias w).
+ * Passing w_out to sgemv_select_groups / sgemv_pack reproduces the same
+ * pruned matrix: their |w| selection keeps every non-zero of a group that
+ * has at most nk non-zeros, and kept zeros dequantise to zero wherever they
+ * sit. Errors: EINVAL (shape, NULL, T < 1 with xcal, non-finite values). */
+int sgemv_prune(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
+                const uint16_t* xcal, int32_t T, uint16_t* w_out);
+
 /* sgemv_pack - dense FP16 W -> N:M prune -> asymmetric INT4 group quantisation
  * -> canonical 2bit-CSR arrays (P1 §1 contributions, first item; §3.2).
  * Pruning keeps, in every group of 4 consecutive columns of a row, the nk

@@ -15,8 +15,10 @@ Modules and what pins each one (tests under ``tests/test_oracle_*.py``):
 
 * ``fp16``   - FP64 -> FP16 round-to-nearest-even; pinned against an exact
                rational rounding of every tie and of random doubles.
-* ``prune``  - N:M selection along K (P1 §3.2 "Sparsification"); pinned by
-               brute force over every kept subset.
+* ``prune``  - N:M selection along K (P1 §3.2 "Sparsification"), by |w| or
+               by the activation-aware score |w| * ||x_k|| of eq. (3);
+               pinned by brute force over every kept subset and a
+               hand-worked group where the two scores disagree.
 * ``groups`` - per-output-channel group size (P1 §3.2 "Adaptive group
                quantization", eq. (3) first term); pinned by exact rational
                sums and ranking on tiny matrices.

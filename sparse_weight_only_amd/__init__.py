@@ -6,6 +6,6 @@ computation runs in that library; Python only marshals arguments, and
 PyTorch only supplies device memory and streams.
 """
 from .sgemv import (  # noqa: F401
-    SgemvError, Desc, Plan, lib, lib_path, describe, select_groups, pack, layout, run, plan, strerror,
+    SgemvError, Desc, Plan, lib, lib_path, describe, select_groups, prune, pack, layout, run, plan, strerror,
     SparseGemvLayer, algorithmic_bytes, Task, MAX_GROUP, run_group, plan_group,
 )

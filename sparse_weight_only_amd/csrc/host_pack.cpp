@@ -3,7 +3,8 @@
 //
 // Follows the page "Efficient LLM ad generation via model compression and
 // parallel verification" (translation of arXiv 2605.11582): §3.2
-// "Sparsification" (layer-wise N:M, 2:4 or 1:4), §3.2 "Adaptive group
+// "Sparsification" (layer-wise N:M, 2:4 or 1:4; the activation-aware
+// importance of eq. (3), first term, in sgemv_prune), §3.2 "Adaptive group
 // quantization" (finer groups for sensitive channels; sensitivity from the
 // first term of eq. (3)), §1 "our core idea" (FP16 -> INT4 weight-only) and
 // the first contribution item (index-compressed 2bit-CSR). Build with
@@ -89,15 +90,8 @@ void quantize_group(const uint16_t* v16, int m, uint16_t* scale16, uint16_t* zer
   *zero16 = f64_to_f16(z);
 }
 
-}  // namespace
-
-extern "C" int sgemv_select_groups(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
-                                   const uint16_t* xcal, int32_t T, double frac_fine,
-                                   int32_t g_fine, int32_t g_coarse, int32_t* group_size_out) {
-  if (!w || !xcal || !group_size_out || !shape_ok(N, K, nk) || T < 1) return SGEMV_EINVAL;
-  if (!(frac_fine >= 0.0 && frac_fine <= 1.0)) return SGEMV_EINVAL;
-  if (!valid_group(g_fine, K) || !valid_group(g_coarse, K)) return SGEMV_EINVAL;
-  if (!all_finite(w, (int64_t)N * K) || !all_finite(xcal, (int64_t)T * K)) return SGEMV_EINVAL;
+// Column scales c_k = sqrt(sum_t xcal[t][k]^2), sequential over t in FP64.
+std::vector<double> column_norms(const uint16_t* xcal, int32_t T, int32_t K) {
   std::vector<double> c(K, 0.0);
   for (int32_t k = 0; k < K; ++k) {
     double s = 0.0;
@@ -107,6 +101,49 @@ extern "C" int sgemv_select_groups(const uint16_t* w, int32_t N, int32_t K, int3
     }
     c[k] = sqrt(s);
   }
+  return c;
+}
+
+}  // namespace
+
+extern "C" int sgemv_prune(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
+                           const uint16_t* xcal, int32_t T, uint16_t* w_out) {
+  if (!w || !w_out || !shape_ok(N, K, nk)) return SGEMV_EINVAL;
+  if (xcal && T < 1) return SGEMV_EINVAL;
+  if (!all_finite(w, (int64_t)N * K)) return SGEMV_EINVAL;
+  if (xcal && !all_finite(xcal, (int64_t)T * K)) return SGEMV_EINVAL;
+  const std::vector<double> c = xcal ? column_norms(xcal, T, K) : std::vector<double>(K, 1.0);
+  for (int32_t n = 0; n < N; ++n) {
+    const uint16_t* row = w + (int64_t)n * K;
+    uint16_t* out = w_out + (int64_t)n * K;
+    for (int32_t j = 0; j < K / 4; ++j) {
+      double sc[4];
+      for (int p = 0; p < 4; ++p) sc[p] = fabs(f16_to_f64(row[4 * j + p])) * c[4 * j + p];
+      // the nk largest scores; a later column replaces an earlier one only
+      // when strictly larger, so ties go to the lower column
+      int first = 0;
+      for (int p = 1; p < 4; ++p)
+        if (sc[p] > sc[first]) first = p;
+      int second = -1;
+      if (nk == 2)
+        for (int p = 0; p < 4; ++p) {
+          if (p == first) continue;
+          if (second < 0 || sc[p] > sc[second]) second = p;
+        }
+      for (int p = 0; p < 4; ++p) out[4 * j + p] = (p == first || p == second) ? row[4 * j + p] : (uint16_t)0;
+    }
+  }
+  return SGEMV_OK;
+}
+
+extern "C" int sgemv_select_groups(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
+                                   const uint16_t* xcal, int32_t T, double frac_fine,
+                                   int32_t g_fine, int32_t g_coarse, int32_t* group_size_out) {
+  if (!w || !xcal || !group_size_out || !shape_ok(N, K, nk) || T < 1) return SGEMV_EINVAL;
+  if (!(frac_fine >= 0.0 && frac_fine <= 1.0)) return SGEMV_EINVAL;
+  if (!valid_group(g_fine, K) || !valid_group(g_coarse, K)) return SGEMV_EINVAL;
+  if (!all_finite(w, (int64_t)N * K) || !all_finite(xcal, (int64_t)T * K)) return SGEMV_EINVAL;
+  const std::vector<double> c = column_norms(xcal, T, K);
   std::vector<double> S(N, 0.0);
   for (int32_t n = 0; n < N; ++n) {
     const uint16_t* row = w + (int64_t)n * K;

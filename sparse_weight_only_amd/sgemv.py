@@ -83,6 +83,7 @@ def lib():
         L.sgemv_describe.argtypes = [i32, i32, i32, P, ctypes.POINTER(Desc)]
         L.sgemv_select_groups.argtypes = [P, i32, i32, i32, P, i32, f64, i32, i32, P]
         L.sgemv_pack.argtypes = [P, i32, i32, i32, P, P, P, P, P, P, P]
+        L.sgemv_prune.argtypes = [P, i32, i32, i32, P, i32, P]
         L.sgemv_layout.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P, P]
         L.sgemv_run.argtypes = [ctypes.POINTER(Desc), P, P, P, i32, P]
         L.sgemv_plan.argtypes = [ctypes.POINTER(Desc), i32, ctypes.POINTER(Plan)]
@@ -90,7 +91,7 @@ def lib():
         L.sgemv_plan_group.argtypes = [ctypes.POINTER(Task), i32, i32, ctypes.POINTER(Plan)]
         L.sgemv_strerror.argtypes = [ctypes.c_int]
         L.sgemv_strerror.restype = ctypes.c_char_p
-        for f in ("sgemv_describe", "sgemv_select_groups", "sgemv_pack", "sgemv_layout", "sgemv_run", "sgemv_plan",
+        for f in ("sgemv_describe", "sgemv_select_groups", "sgemv_pack", "sgemv_prune", "sgemv_layout", "sgemv_run", "sgemv_plan",
                   "sgemv_run_group", "sgemv_plan_group"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -135,6 +136,22 @@ def select_groups(w16: np.ndarray, nk: int, xcal16: np.ndarray, frac_fine: float
     _check(lib().sgemv_select_groups(_ptr(w), N, K, nk, _ptr(xc), xc.shape[0], float(frac_fine),
                                      g_fine, g_coarse, _ptr(out)), "sgemv_select_groups")
     return out
+
+
+def prune(w16: np.ndarray, nk: int, xcal16=None) -> np.ndarray:
+    """Activation-aware N:M pruning (score |w| * ||x_k||; |w| without xcal):
+    FP16 [N, K] with the kept values and +0 elsewhere."""
+    w = _host(np.asarray(w16).view(np.uint16), np.uint16)
+    N, K = w.shape
+    out = np.empty((N, K), dtype=np.uint16)
+    if xcal16 is None:
+        _check(lib().sgemv_prune(_ptr(w), N, K, nk, None, 0, _ptr(out)), "sgemv_prune")
+    else:
+        xc = _host(np.asarray(xcal16).view(np.uint16), np.uint16)
+        if xc.ndim != 2 or xc.shape[1] != K:
+            raise ValueError("xcal must be [T, K]")
+        _check(lib().sgemv_prune(_ptr(w), N, K, nk, _ptr(xc), xc.shape[0], _ptr(out)), "sgemv_prune")
+    return out.view(np.float16)
 
 
 def pack(w16: np.ndarray, nk: int, group_size) -> dict:

@@ -263,3 +263,24 @@ def test_group_launch_decoder_layer():
             if len(grp) == 1:
                 # a group of one is the single call: same kernel, same geometry, same bits
                 assert np.array_equal(y.view(np.uint16), run_checked(layer, L.X(1)).view(np.uint16))
+
+
+@pytest.mark.parametrize("nk", [2, 1])
+def test_activation_aware_pruned_layer(nk):
+    """Weights pruned by |w| * ||x_k|| (sgemv_prune) through pack, layout and the
+    kernel, against the oracle's scored selection quantised and multiplied in FP64."""
+    from oracle import prune as oprune, pack as opack
+    L = synth.cfg2()[0]
+    W = L.W()
+    Xall = L.X(72)
+    Xcal, X = Xall[:64], Xall[64:]
+    Wp = sg.prune(W, nk, Xcal)
+    gs = sg.select_groups(Wp, nk, Xcal)
+    say(f"case activation-aware pruning nk={nk}")
+    layer = make_layer(Wp, nk, gs)
+    co = opack.pack_canonical(oprune.pruned_dense(W, oprune.nm_prune_scored(W, nk, Xcal)[1]), nk, gs)
+    Wd = ogemv.dequant_dense(co)
+    y = run_checked(layer, X)
+    err = ogemv.normalized_error(y, ogemv.gemv(Wd, X), ogemv.abs_dot(Wd, X))
+    say(f"  normalised error {err:.3e}")
+    assert err <= TOL

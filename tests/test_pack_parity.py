@@ -281,3 +281,63 @@ def test_group_plan_and_host_errors():
         with pytest.raises(sg.SgemvError) as e:
             sg.run_group(fake([small]) + [task], 1)
         assert e.value.code == code
+
+
+@pytest.mark.parametrize("nk", [1, 2])
+def test_prune_scored_matches_oracle(nk):
+    """sgemv_prune (C++) against oracle.prune.nm_prune_scored, bit for bit, on
+    random, tie-heavy and outlier-channel inputs, with and without a
+    calibration batch."""
+    from oracle import prune as oprune
+    rng = np.random.default_rng(31 + nk)
+    pool = np.array([0.0, -0.0, 0.5, -0.5, 1.0, 0.25, -2.0], dtype=np.float16)
+    cases = [((rng.standard_normal((40, 512)) * 0.02).astype(np.float16), rng.standard_normal((8, 512)).astype(np.float16)),
+             (pool[rng.integers(0, len(pool), (33, 256))], pool[rng.integers(0, len(pool), (3, 256))]),
+             (synth.cfg2()[0].W()[:64], synth.cfg2()[0].X(4)),                # 41 channels x20
+             ((rng.standard_normal((9, 256)) * 0.02).astype(np.float16), np.zeros((2, 256), np.float16))]
+    for W, X in cases:
+        for xc in (X, None):
+            got = sg.prune(W, nk, xc)
+            want = oprune.pruned_dense(W, oprune.nm_prune_scored(W, nk, xc)[1])
+            assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+    with pytest.raises(sg.SgemvError):
+        sg.prune(np.full((4, 256), np.nan, np.float16), nk)
+    with pytest.raises(sg.SgemvError):
+        sg.prune(np.zeros((4, 256), np.float16), nk, np.full((1, 256), np.inf, np.float16))
+
+
+def test_pack_of_pruned_matrix_keeps_the_pruned_weights():
+    """sgemv_pack on sgemv_prune's output dequantises to the same matrix as
+    quantising the scored selection directly (oracle)."""
+    from oracle import prune as oprune, quant as oquant, gemv as ogemv
+    L = synth.cfg2()[0]
+    W = L.W()[:96]
+    X = L.Xcal(synth.CALIB_T)
+    for nk in (1, 2):
+        Wp = sg.prune(W, nk, X)
+        gs = sg.select_groups(Wp, nk, X)
+        canon = sg.pack(Wp, nk, gs)
+        Wd = ogemv.dequant_dense(canon)
+        # oracle: scored selection, then the same quantiser on the kept values
+        offs, mask = oprune.nm_prune_scored(W, nk, X)
+        co = opack.pack_canonical(oprune.pruned_dense(W, mask), nk, gs)
+        assert np.array_equal(ogemv.dequant_dense(co), Wd)
+        assert np.all(Wd[~mask] == 0)
+
+
+def test_activation_aware_pruning_lowers_output_error_with_outlier_channels():
+    """On the 4096 x 4096 workload (41 input channels x20) the |w| * ||x||
+    selection keeps the outlier channels' weights and so approximates the
+    dense product better than |w| alone (measured on the oracle)."""
+    from oracle import prune as oprune
+    L = synth.cfg2()[0]
+    W = L.W()[:256]
+    Xall = L.X(72)                       # calibration rows and test rows share the outlier channels
+    Xcal, X = Xall[:64], Xall[64:]
+    dense = X.astype(np.float64) @ W.astype(np.float64).T
+    for nk in (1, 2):
+        errs = {}
+        for name, xc in (("magnitude", None), ("activation_aware", Xcal)):
+            Wp = oprune.pruned_dense(W, oprune.nm_prune_scored(W, nk, xc)[1]).astype(np.float64)
+            errs[name] = np.linalg.norm(X.astype(np.float64) @ Wp.T - dense) / np.linalg.norm(dense)
+        assert errs["activation_aware"] < errs["magnitude"], errs
