@@ -21,6 +21,11 @@ Timing protocol
   one pass over the same four layers.
 
 Beside the step, the same line reports
+* ``ablation``: the up and down MLP weights as a dense INT4 layer (every
+  element kept, same quantiser: the plain weight-only GEMV that SparseGemv
+  extends) and as a plain FP16 GEMV through torch (hipBLASLt, launched
+  eagerly: a library call stays out of graph capture), at B = 1, cold, with
+  the sparse layers' speedups;
 * ``beam``: µs and GB/s per call of the beam-batch shapes (up and down of
   decoder layers 0 (2:4) and 4 (1:4)) at B = 4, 8, 16, timed like the
   per-layer figures;
@@ -65,6 +70,7 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a HIP graph")
     ap.add_argument("--no-beam", action="store_true", help="skip the beam-batch figures")
     ap.add_argument("--no-decoder", action="store_true", help="skip the 224-GEMV decoder sequence")
+    ap.add_argument("--no-ablation", action="store_true", help="skip the dense INT4 / FP16 ablation")
     return ap.parse_args()
 
 
@@ -283,6 +289,60 @@ def main():
             torch.cuda.empty_cache()
         log("beam batches timed")
 
+    # ---- ablation at B = 1: the same MLP weights as a dense INT4 layer (every
+    # element kept, same quantiser and groups policy) and as a plain FP16
+    # GEMV through torch (hipBLASLt), each timed cold like the sparse layers
+    ablation = None
+    if not args.no_ablation:
+        import dataclasses
+        ablation = {}
+        for L in [L for L in layers if L.nk == 2]:
+            Ld = dataclasses.replace(L, nk=4)
+            W = Ld.W()
+            gs = sg.select_groups(W, 4, Ld.Xcal(synth.CALIB_T), synth.FRAC_FINE, synth.G_FINE, synth.G_COARSE)
+            desc = sg.describe(Ld.N, Ld.K, 4, gs)
+            host = torch.from_numpy(sg.layout(desc, sg.pack(W, 4, gs)))
+            R = max(2, -(-COLD_BYTES // desc.blob_bytes))
+            copies = [host.to(dev) for _ in range(R)]
+            x = torch.from_numpy(Ld.X(1)).to(dev)
+            y = torch.empty((1, Ld.N), dtype=torch.float16, device=dev)
+            us_d = per_call_us(desc, copies, x, y, 1, args.layer_calls)
+            nb_d = sg.algorithmic_bytes(desc, 1)
+            del copies
+            w16 = torch.from_numpy(W).to(dev)
+            R16 = max(2, -(-COLD_BYTES // (w16.numel() * 2)))
+            wcopies = [w16.clone() for _ in range(R16)]
+            n16 = R16 * max(1, args.layer_calls // (R16 * 4))
+
+            # launched eagerly (a library GEMV is kept out of graph capture);
+            # each call takes longer on the GPU than its host dispatch
+            for i in range(R16):
+                torch.nn.functional.linear(x, wcopies[i])
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            cur = torch.cuda.current_stream(dev)
+            e0.record(cur)
+            for i in range(n16):
+                torch.nn.functional.linear(x, wcopies[i % R16])
+            e1.record(cur)
+            torch.cuda.synchronize()
+            us_h = e0.elapsed_time(e1) * 1e3 / n16
+            nb_h = w16.numel() * 2 + 2 * Ld.K + 2 * Ld.N
+            del wcopies, w16
+            torch.cuda.empty_cache()
+            base = L.name.replace("_2of4", "")
+            s24 = per_layer[base + "_2of4"]["us_per_call"]
+            s14 = per_layer[base + "_1of4"]["us_per_call"]
+            ablation[base] = {
+                "dense_int4": {"us_per_call": round(us_d, 3), "bytes": nb_d, "GBps": round(nb_d / (us_d * 1e-6) / 1e9, 1)},
+                "fp16_torch_linear": {"us_per_call": round(us_h, 3), "bytes": nb_h,
+                                      "GBps": round(nb_h / (us_h * 1e-6) / 1e9, 1)},
+                "speedup_2of4_vs_dense_int4": round(us_d / s24, 3),
+                "speedup_1of4_vs_dense_int4": round(us_d / s14, 3),
+                "speedup_2of4_vs_fp16": round(us_h / s24, 3),
+                "speedup_1of4_vs_fp16": round(us_h / s14, 3)}
+        log("ablation timed")
+
     # ---- 224-GEMV decoder sequence, one launch per GEMV
     decoder = None
     if not args.no_decoder:
@@ -358,6 +418,8 @@ def main():
         out["beam"] = beam
     if decoder is not None:
         out["decoder"] = decoder
+    if ablation is not None:
+        out["ablation"] = ablation
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layers_host)
     print(json.dumps(out), flush=True)

@@ -44,7 +44,7 @@ enum {
  * passed back by pointer; the caller may copy it freely. */
 typedef struct sgemv_desc {
   int32_t N, K;          /* output rows, input columns (K % 256 == 0)                  */
-  int32_t nk;            /* kept elements per group of 4 along K: 2 (2:4) or 1 (1:4)   */
+  int32_t nk;            /* kept per group of 4 along K: 2 (2:4), 1 (1:4), 4 (dense)   */
   int32_t n_blocks;      /* row blocks of 16 rows (rows sorted by group size)          */
   int32_t chunks;        /* column chunks of 256 dense columns per row: K / 256        */
   int32_t g_min, g_max;  /* smallest and largest group size present                    */
@@ -52,7 +52,7 @@ typedef struct sgemv_desc {
   int32_t reserved;      /* zero                                                       */
   int64_t kept;          /* N*K*nk/4 kept elements                                     */
   int64_t vals_bytes;    /* canonical code array: kept/2 bytes (one nibble each)       */
-  int64_t offs_bytes;    /* canonical offset array: kept/4 bytes (2 bits each)         */
+  int64_t offs_bytes;    /* canonical offset array: kept/4 bytes (2 bits each); 0 dense */
   int64_t n_groups;      /* sum_n K/g_n: one FP16 scale and one FP16 zero each         */
   int64_t off_codes;     /* byte offsets of the blob sections (256-byte aligned)       */
   int64_t off_offs;
@@ -64,7 +64,11 @@ typedef struct sgemv_desc {
 /* sgemv_describe - validate a layer shape and fill its descriptor.
  *   N, K         : rows and columns; N >= 1, K >= 256, K % 256 == 0, K <= 32768,
  *                  and the blob must stay below 2^31 bytes.
- *   nk           : 2 for 2:4 or 1 for 1:4 (P1 §3.2 "Sparsification").
+ *   nk           : 2 for 2:4 or 1 for 1:4 (P1 §3.2 "Sparsification"); 4 for
+ *                  the dense INT4 ablation (every element kept, no offsets:
+ *                  the plain weight-only GEMV that SparseGemv extends, P1 §1
+ *                  contributions, second item), which sgemv_pack,
+ *                  sgemv_layout and sgemv_run accept as well.
  *   group_size   : host int32[N], group size of each row in dense columns; each
  *                  in {32, 64, 128, 256} (P1 §3.2 "Adaptive group quantization":
  *                  finer groups for sensitive channels).
@@ -116,7 +120,8 @@ int sgemv_prune(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
  * zero, 0, 15); FP64 arithmetic, round half to even.
  * Output arrays (host, caller-sized from the descriptor):
  *   vals  [N][K*nk/8]  element j of a row in byte j/2, low nibble when j is even;
- *   offs  [N][K*nk/16] in-group offset of element j in byte j/4, bits 2(j%4)..+1;
+ *   offs  [N][K*nk/16] in-group offset of element j in byte j/4, bits 2(j%4)..+1
+ *                      (none, and offs may be NULL, for the dense nk = 4);
  *   scale, zero [n_groups] FP16 bits, row-major over (row, group);
  *   gptr  [N+1] first group of each row; rowptr [N+1] = n*K*nk/4.
  * Errors: EINVAL (shape, group sizes, NULL, non-finite weight). */

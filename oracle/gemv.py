@@ -15,6 +15,8 @@ def dequant_dense(canon: dict) -> np.ndarray:
     N, K, nk = canon["N"], canon["K"], canon["nk"]
     gs = np.asarray(canon["group_size"], dtype=np.int64)
     q, o = unpack_bytes(canon["vals"], canon["offs"])
+    if nk == 4:                                   # dense: no stored offsets
+        o = np.tile(np.arange(4, dtype=np.uint8), (N, K // 4))
     s = from_bits(canon["scale"])
     z = from_bits(canon["zero"])
     gptr = np.asarray(canon["gptr"], dtype=np.int64)

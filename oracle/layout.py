@@ -27,6 +27,14 @@ Bits of a piece
   element m at bit 16*((m//4) % 2) + (REAL if m//4 < 2 else DUMMY)[m % 4],
   REAL = [0,4,10,14], DUMMY = [2,6,8,12].
 
+Dense ablation (nk = 4, every element kept, no offsets): a piece holds the
+64 elements of its columns in 8 dwords; dword 2t + h (t = 0..3, h = 0, 1)
+holds, for the 4 groups of columns 16t .. 16t + 15 of the piece, the
+elements at in-group positions 2h and 2h + 1: dword element k = 2g + p'
+(group g, position 2h + p') at nibble NIB[2][k], so that each dword is a
+2-of-4 operand whose index field is the constant (0, 1) or (2, 3) per
+group. The offset section is empty.
+
 Scale/zero: one 32-bit word per group, FP16 scale in the low half, FP16 zero
 in the high half; records (b, c) in (b, c) order, each listing the rows of
 block b in order, each row with its 256/g words of chunk c (its groups
@@ -60,12 +68,23 @@ def off14_bit(m: int) -> int:
     return 16 * (t % 2) + (REAL if t < 2 else DUMMY)[e]
 
 
+def piece_offs_bytes(nk: int) -> int:
+    return 0 if nk == 4 else 4 * nk
+
+
+def dense_dword_element(d: int, k: int) -> int:
+    """Element (0..63) of a dense piece held by element k of code dword d."""
+    t, h = divmod(d, 2)
+    g, pp = divmod(k, 2)
+    return 16 * t + 4 * g + 2 * h + pp
+
+
 def section_offsets(N: int, K: int, nk: int, n_groups: int) -> dict:
     T, C = -(-N // 16), K // 256
     records = T * C * 64
     off = {"codes": 0}
     off["offs"] = _align(records * 8 * nk)
-    off["perm"] = _align(off["offs"] + records * 4 * nk)
+    off["perm"] = _align(off["offs"] + records * piece_offs_bytes(nk))
     off["sz"] = _align(off["perm"] + 4 * 16 * T)
     off["blob_bytes"] = _align(off["sz"] + 4 * n_groups + 8)
     return off
@@ -77,6 +96,8 @@ def build(canon: dict) -> dict:
     gs = np.asarray(canon["group_size"], dtype=np.int64)
     T, C, kpp = -(-N // 16), K // 256, 16 * nk
     q, o = unpack_bytes(canon["vals"], canon["offs"])           # [N, K*nk/4] each
+    if nk == 4:
+        o = np.zeros_like(q)                                     # no offsets stored
     sz_all = (np.asarray(canon["scale"], dtype=np.uint32)
               | (np.asarray(canon["zero"], dtype=np.uint32) << np.uint32(16)))
     gptr = np.asarray(canon["gptr"], dtype=np.int64)
@@ -85,12 +106,19 @@ def build(canon: dict) -> dict:
     qs = q[perm].astype(np.uint32).reshape(N, C, 4, kpp)
     os_ = o[perm].astype(np.uint32).reshape(N, C, 4, kpp)
     # codes: dwords of 8 elements, element k at nibble NIB[k]
-    qd = qs.reshape(N, C, 4, kpp // 8, 8)
     cw = np.zeros((N, C, 4, kpp // 8), dtype=np.uint32)
-    for k in range(8):
-        cw |= qd[..., k] << np.uint32(4 * NIB[nk][k])
+    if nk == 4:
+        for d in range(8):
+            for k in range(8):
+                cw[..., d] |= qs[..., dense_dword_element(d, k)] << np.uint32(4 * NIB[2][k])
+    else:
+        qd = qs.reshape(N, C, 4, kpp // 8, 8)
+        for k in range(8):
+            cw |= qd[..., k] << np.uint32(4 * NIB[nk][k])
     # offsets
-    if nk == 2:
+    if nk == 4:
+        ow = np.zeros((N, C, 4, 0), dtype=np.uint32)
+    elif nk == 2:
         od = os_.reshape(N, C, 4, 2, 16)
         ow = np.zeros((N, C, 4, 2), dtype=np.uint32)
         for m in range(16):
@@ -144,7 +172,8 @@ def decode(blob: np.ndarray, N: int, K: int, nk: int, group_size):
     u32 = lambda at, n: np.frombuffer(blob[at: at + 4 * n].tobytes(), dtype="<u4")
     perm = np.frombuffer(blob[off["perm"]: off["perm"] + 64 * T].tobytes(), dtype="<i4")
     cw = u32(off["codes"], T * C * 64 * 2 * nk).reshape(T, C, 64, 2 * nk)
-    ow = u32(off["offs"], T * C * 64 * nk).reshape(T, C, 64, nk)
+    now = piece_offs_bytes(nk) // 4
+    ow = u32(off["offs"], T * C * 64 * now).reshape(T, C, 64, now)
     szw = u32(off["sz"], n_groups)
     kpr = K * nk // 4
     q = np.zeros((N, kpr), dtype=np.uint8)
@@ -161,6 +190,11 @@ def decode(blob: np.ndarray, N: int, K: int, nk: int, group_size):
                 for qq in range(4):
                     lane = r + 16 * qq
                     e0 = kpp * (4 * c + qq)
+                    if nk == 4:
+                        for d in range(8):
+                            for k in range(8):
+                                q[n, e0 + dense_dword_element(d, k)] = (cw[b, c, lane, d] >> (4 * NIB[2][k])) & 0xF
+                        continue
                     for m in range(kpp):
                         dw, k = divmod(m, 8)
                         q[n, e0 + m] = (cw[b, c, lane, dw] >> (4 * NIB[nk][k])) & 0xF

@@ -14,6 +14,11 @@ column, j = 0 .. K*nk/4 - 1, column 4*(j // nk) + off_j):
   scale/zero arrays: sum over earlier rows of K/g_m);
 * rowptr int32 [N+1] first kept element of row n (n*K*nk/4; regular because
   every group of 4 keeps exactly nk elements).
+
+nk = 4 is the dense INT4 ablation (the plain weight-only GEMV that
+SparseGemv extends, P1 §1 contributions, second item): every element is
+kept, element j is column j, and no offsets are stored (``offs`` has zero
+bytes per row).
 """
 import numpy as np
 
@@ -28,7 +33,7 @@ def sizes(N: int, K: int, nk: int, group_size) -> dict:
     return {
         "kept": kept,
         "vals_bytes": kept // 2,
-        "offs_bytes": kept // 4,
+        "offs_bytes": 0 if nk == 4 else kept // 4,
         "n_groups": int(np.sum(K // gs)),
     }
 
@@ -89,6 +94,8 @@ def pack_canonical(W16: np.ndarray, nk: int, group_size) -> dict:
     q, scale, zero, gptr = quantize_rows(kept16, nk, K, gs)
     o = offs3.reshape(N, -1)
     vals, offs = pack_bytes(q, o)
+    if nk == 4:
+        offs = np.zeros((N, 0), dtype=np.uint8)      # dense: column j is element j
     kpr = K * nk // 4
     return {
         "N": N, "K": K, "nk": nk, "group_size": gs.astype(np.int32),

@@ -14,7 +14,8 @@ import numpy as np
 def nm_prune(W16: np.ndarray, nk: int):
     """Select the kept elements of every group of 4 along K.
 
-    W16: FP16 [N, K] (row = output channel), K % 4 == 0; nk in {1, 2}.
+    W16: FP16 [N, K] (row = output channel), K % 4 == 0; nk in {1, 2}, or 4
+         for the dense (unpruned) ablation, which keeps every element.
     Returns (offs, mask):
       offs: uint8 [N, K//4, nk]  in-group column offsets of the kept
             elements, ascending;
@@ -22,8 +23,8 @@ def nm_prune(W16: np.ndarray, nk: int):
     """
     W = np.asarray(W16, dtype=np.float16)
     N, K = W.shape
-    if K % 4 or nk not in (1, 2):
-        raise ValueError("K must be a multiple of 4 and nk in {1, 2}")
+    if K % 4 or nk not in (1, 2, 4):
+        raise ValueError("K must be a multiple of 4 and nk in {1, 2, 4}")
     if not np.all(np.isfinite(W)):
         raise ValueError("non-finite weight")
     a = np.abs(W.astype(np.float64)).reshape(N, K // 4, 4)

@@ -16,6 +16,9 @@
 //  - offsets of a piece: 2:4 = the canonical 2-bit fields (element m at bits
 //    2m of a little-endian 64-bit word); 1:4 = one dword, element m at bit
 //    16*((m/4)%2) + (m/4 < 2 ? [0,4,10,14] : [2,6,8,12])[m%4];
+//  - dense ablation (nk = 4, no offsets): code dword 2t + h holds positions
+//    2h and 2h + 1 of the 4 groups of piece columns 16t .. 16t + 15, element
+//    k = 2g + p at nibble [0,4,1,5,2,6,3,7][k];
 //  - perm: original row of each sorted row, -1 for padding rows;
 //  - scale|zero<<16 words: records (b, c) in order, each the rows of block b
 //    in order, each with its 256/g words of chunk c (groups c*256/g ..).
@@ -51,7 +54,7 @@ constexpr int kOff14Dummy[4] = {2, 6, 8, 12};
 extern "C" int sgemv_describe(int32_t N, int32_t K, int32_t nk, const int32_t* group_size,
                               sgemv_desc* out) {
   if (!group_size || !out) return SGEMV_EINVAL;
-  if (N < 1 || K < kChunkCols || K % kChunkCols != 0 || (nk != 1 && nk != 2)) return SGEMV_EINVAL;
+  if (N < 1 || K < kChunkCols || K % kChunkCols != 0 || !valid_nk(nk)) return SGEMV_EINVAL;
   if (K / kChunkCols > kMaxChunks) return SGEMV_ESIZE;
   int g_min = 1 << 30, g_max = 0;
   int64_t n_groups = 0;
@@ -72,7 +75,7 @@ extern "C" int sgemv_describe(int32_t N, int32_t K, int32_t nk, const int32_t* g
   d.g_min = g_min; d.g_max = g_max;
   d.kept = (int64_t)N * K * nk / 4;
   d.vals_bytes = d.kept / 2;
-  d.offs_bytes = d.kept / 4;
+  d.offs_bytes = nk == 4 ? 0 : d.kept / 4;
   d.n_groups = n_groups;
   const int64_t records = (int64_t)T * C * 64;
   d.off_codes = 0;
@@ -89,9 +92,9 @@ extern "C" int sgemv_describe(int32_t N, int32_t K, int32_t nk, const int32_t* g
 extern "C" int sgemv_layout(const sgemv_desc* d, const uint8_t* vals, const uint8_t* offs,
                             const uint16_t* scale, const uint16_t* zero, const int32_t* gptr,
                             void* blob_v) {
-  if (!d || !vals || !offs || !scale || !zero || !gptr || !blob_v) return SGEMV_EINVAL;
+  if (!d || !vals || (!offs && d->nk != 4) || !scale || !zero || !gptr || !blob_v) return SGEMV_EINVAL;
   const int32_t N = d->N, K = d->K, nk = d->nk;
-  if (N < 1 || K < kChunkCols || K % kChunkCols || (nk != 1 && nk != 2)) return SGEMV_EINVAL;
+  if (N < 1 || K < kChunkCols || K % kChunkCols || !valid_nk(nk)) return SGEMV_EINVAL;
   // group sizes from the ragged row pointer of the scale/zero arrays
   std::vector<int32_t> gs(N);
   if (gptr[0] != 0) return SGEMV_EINVAL;
@@ -140,10 +143,24 @@ extern "C" int sgemv_layout(const sgemv_desc* d, const uint8_t* vals, const uint
         if (i >= N) break;
         const int32_t n = perm[i];
         const uint8_t* vrow = vals + (int64_t)n * (kpr / 2);
-        const uint8_t* orow = offs + (int64_t)n * (kpr / 4);
+        const uint8_t* orow = nk == 4 ? nullptr : offs + (int64_t)n * (kpr / 4);
         for (int q = 0; q < 4; ++q) {
           const int64_t rec = ((int64_t)b * C + c) * 64 + r + 16 * q;
           const int64_t e0 = (int64_t)kpp * (4 * c + q);        // first kept element of the piece
+          if (nk == 4) {
+            // dense: dword 2t + h holds in-group positions 2h, 2h + 1 of the 4
+            // groups of columns 16t .. 16t + 15 (a 2-of-4 operand each)
+            for (int dw = 0; dw < 8; ++dw) {
+              uint32_t word = 0;
+              for (int k = 0; k < 8; ++k) {
+                const int64_t j = e0 + 16 * (dw / 2) + 4 * (k / 2) + 2 * (dw % 2) + (k % 2);
+                const uint32_t code = (vrow[j >> 1] >> (4 * (j & 1))) & 0xFu;
+                word |= code << (4 * kNib24[k]);
+              }
+              memcpy(cb + rec * pcb + 4 * dw, &word, 4);
+            }
+            continue;
+          }
           // codes: dwords of 8 elements with the nibble order of the N:M choice
           for (int dw = 0; dw < pcb / 4; ++dw) {
             uint32_t word = 0;

@@ -23,13 +23,17 @@ using namespace sgemv;
 namespace {
 
 bool shape_ok(int32_t N, int32_t K, int32_t nk) {
-  if (N < 1 || K < 256 || K % 256 != 0 || (nk != 1 && nk != 2)) return false;
+  if (N < 1 || K < 256 || K % 256 != 0 || !valid_nk(nk)) return false;
   return (int64_t)N * K * nk / 4 < ((int64_t)1 << 31);
 }
 
 // Kept offsets of one group of 4 (ascending): the nk largest |w|, lower
 // column first among equal magnitudes (-0 equals +0).
 inline void select_kept(const uint16_t* g4, int nk, int* out) {
+  if (nk == 4) {                  // dense ablation: every element
+    for (int p = 0; p < 4; ++p) out[p] = p;
+    return;
+  }
   uint16_t mag[4];
   for (int p = 0; p < 4; ++p) mag[p] = (uint16_t)(g4[p] & 0x7FFFu);   // finite: ordered like |w|
   int first = 0;
@@ -108,7 +112,7 @@ std::vector<double> column_norms(const uint16_t* xcal, int32_t T, int32_t K) {
 
 extern "C" int sgemv_prune(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
                            const uint16_t* xcal, int32_t T, uint16_t* w_out) {
-  if (!w || !w_out || !shape_ok(N, K, nk)) return SGEMV_EINVAL;
+  if (!w || !w_out || !shape_ok(N, K, nk) || nk == 4) return SGEMV_EINVAL;
   if (xcal && T < 1) return SGEMV_EINVAL;
   if (!all_finite(w, (int64_t)N * K)) return SGEMV_EINVAL;
   if (xcal && !all_finite(xcal, (int64_t)T * K)) return SGEMV_EINVAL;
@@ -149,7 +153,7 @@ extern "C" int sgemv_select_groups(const uint16_t* w, int32_t N, int32_t K, int3
     const uint16_t* row = w + (int64_t)n * K;
     double s = 0.0;
     for (int32_t j = 0; j < K / 4; ++j) {
-      int kept[2];
+      int kept[4];
       select_kept(row + 4 * j, nk, kept);
       // columns in ascending order; pruned columns add +0 and are skipped
       for (int i = 0; i < nk; ++i) {
@@ -171,7 +175,7 @@ extern "C" int sgemv_select_groups(const uint16_t* w, int32_t N, int32_t K, int3
 extern "C" int sgemv_pack(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
                           const int32_t* group_size, uint8_t* vals, uint8_t* offs,
                           uint16_t* scale, uint16_t* zero, int32_t* gptr, int32_t* rowptr) {
-  if (!w || !group_size || !vals || !offs || !scale || !zero || !gptr || !rowptr) return SGEMV_EINVAL;
+  if (!w || !group_size || !vals || (!offs && nk != 4) || !scale || !zero || !gptr || !rowptr) return SGEMV_EINVAL;
   if (!shape_ok(N, K, nk)) return SGEMV_EINVAL;
   for (int32_t n = 0; n < N; ++n)
     if (!valid_group(group_size[n], K)) return SGEMV_EINVAL;
@@ -183,7 +187,7 @@ extern "C" int sgemv_pack(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
   for (int32_t n = 0; n < N; ++n) {
     const uint16_t* row = w + (int64_t)n * K;
     for (int32_t j = 0; j < K / 4; ++j) {
-      int kept[2];
+      int kept[4];
       select_kept(row + 4 * j, nk, kept);
       for (int i = 0; i < nk; ++i) {
         kv[j * nk + i] = row[4 * j + kept[i]];
@@ -198,6 +202,10 @@ extern "C" int sgemv_pack(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
     gbase += K / g;
     uint8_t* vrow = vals + (int64_t)n * (kpr / 2);
     for (int j = 0; j < kpr / 2; ++j) vrow[j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
+    if (nk == 4) {                            // dense: no offsets
+      rowptr[n] = (int32_t)((int64_t)n * kpr);
+      continue;
+    }
     uint8_t* orow = offs + (int64_t)n * (kpr / 4);
     for (int j = 0; j < kpr / 4; ++j)
       orow[j] = (uint8_t)(ko[4 * j] | (ko[4 * j + 1] << 2) | (ko[4 * j + 2] << 4) | (ko[4 * j + 3] << 6));

@@ -67,8 +67,10 @@ constexpr int kMaxChunksPerWave = 8;       // register budget of the kernel
 inline int bucket(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
 
 // Bytes of one piece (one row, 64 dense columns) in the code and offset sections.
-inline int piece_code_bytes(int nk) { return 8 * nk; }    // 16 kept (1:4) or 32 kept (2:4) nibbles
-inline int piece_offs_bytes(int nk) { return 4 * nk; }    // 2 bits per kept element
+// nk = 4 is the dense ablation: every element kept, no offsets stored.
+inline bool valid_nk(int nk) { return nk == 1 || nk == 2 || nk == 4; }
+inline int piece_code_bytes(int nk) { return 8 * nk; }    // 16 (1:4), 32 (2:4) or 64 (dense) nibbles
+inline int piece_offs_bytes(int nk) { return nk == 4 ? 0 : 4 * nk; }   // 2 bits per kept element
 
 // Launch geometry for (chunks per row, row blocks, batch): how the column
 // chunks of a row block are split over the waves of its workgroup and how

@@ -12,14 +12,18 @@ typedef void (*GroupFn)(GParams);
 // loads per lane and phase (each in {1, 2, 4, 8}); nullptr otherwise.
 KernelFn get_kernel_nk1(int imax, int xmax);
 KernelFn get_kernel_nk2(int imax, int xmax);
+KernelFn get_kernel_nk4(int imax, int xmax);
 inline KernelFn get_kernel(int nk, int imax, int xmax) {
-  return nk == 2 ? get_kernel_nk2(imax, xmax) : nk == 1 ? get_kernel_nk1(imax, xmax) : nullptr;
+  return nk == 2 ? get_kernel_nk2(imax, xmax) : nk == 1 ? get_kernel_nk1(imax, xmax)
+       : nk == 4 ? get_kernel_nk4(imax, xmax) : nullptr;
 }
 // The same for the several-layer launch.
 GroupFn get_group_kernel_nk1(int imax, int xmax);
 GroupFn get_group_kernel_nk2(int imax, int xmax);
+GroupFn get_group_kernel_nk4(int imax, int xmax);
 inline GroupFn get_group_kernel(int nk, int imax, int xmax) {
-  return nk == 2 ? get_group_kernel_nk2(imax, xmax) : nk == 1 ? get_group_kernel_nk1(imax, xmax) : nullptr;
+  return nk == 2 ? get_group_kernel_nk2(imax, xmax) : nk == 1 ? get_group_kernel_nk1(imax, xmax)
+       : nk == 4 ? get_group_kernel_nk4(imax, xmax) : nullptr;
 }
 
 }  // namespace sgemv_dev

@@ -45,6 +45,7 @@ namespace sgemv_dev {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h16 __attribute__((ext_vector_type(16)));
@@ -186,7 +187,7 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
   __builtin_amdgcn_sched_barrier(0);
 
   // weights of every chunk of the wave
-  typedef typename std::conditional<NK == 2, u32x4, u32x2>::type CodeT;
+  typedef typename std::conditional<NK == 4, u32x8, typename std::conditional<NK == 2, u32x4, u32x2>::type>::type CodeT;
   typedef typename std::conditional<NK == 2, u32x2, uint32_t>::type OffT;
   CodeT cv[IMAX];
   OffT ov[IMAX];
@@ -197,7 +198,13 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
     const bool ok = i < ncw;
     const uint32_t rec = (uint32_t)(rb * p.C + c) * 64u + lane;
     const uint32_t so = p.off_sz + (sz_block + (uint32_t)c * rec_words + sz_lane) * 4u;
-    if constexpr (NK == 2) {
+    if constexpr (NK == 4) {
+      // dense ablation: 32 bytes of codes, no offsets
+      const u32x4 lo = bload4<kStream>(rbuf, ok ? p.off_codes + rec * CB : kOutOfRange);
+      const u32x4 hi = bload4<kStream>(rbuf, ok ? p.off_codes + rec * CB + 16u : kOutOfRange);
+      cv[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      ov[i] = 0u;
+    } else if constexpr (NK == 2) {
       cv[i] = bload4<kStream>(rbuf, ok ? p.off_codes + rec * CB : kOutOfRange);
       ov[i] = bload2<kStream>(rbuf, ok ? p.off_offs + rec * OB : kOutOfRange);
     } else {
@@ -240,6 +247,22 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const Deq& d = t < 2 ? d0 : d1;
+      const h8 blo = *reinterpret_cast<const h8*>(xc + 16 * t);
+      const h8 bhi = *reinterpret_cast<const h8*>(xc + 16 * t + 128);
+      const h16 Bop = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      if constexpr (NK == 4) {
+        // dense ablation: the 4 groups of step t as two 2-of-4 operands with
+        // constant index fields, in-group positions (0, 1) and (2, 3)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t cw = cv[i][2 * t + h], c8 = cw >> 8;
+          const h2 A0 = as_h2(deq_lo(cw, magic, d)), A1 = as_h2(deq_hi(cw, magic, d));
+          const h2 A2 = as_h2(deq_lo(c8, magic, d)), A3 = as_h2(deq_hi(c8, magic, d));
+          const h8 A = {A0.x, A0.y, A1.x, A1.y, A2.x, A2.y, A3.x, A3.y};
+          acc = smfmac<0>(A, Bop, acc, h ? 0xEEEEEEEEu : 0x44444444u);
+        }
+        continue;
+      }
       uint32_t a0, a1, a2, a3, idx;
       if constexpr (NK == 2) {
         // step t: code dword t = 8 kept elements, 2 per group of 4 columns
@@ -264,9 +287,6 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
       }
       const h2 A0 = as_h2(a0), A1 = as_h2(a1), A2 = as_h2(a2), A3 = as_h2(a3);
       const h8 A = {A0.x, A0.y, A1.x, A1.y, A2.x, A2.y, A3.x, A3.y};
-      const h8 blo = *reinterpret_cast<const h8*>(xc + 16 * t);
-      const h8 bhi = *reinterpret_cast<const h8*>(xc + 16 * t + 128);
-      const h16 Bop = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
       if (t & 1) acc = smfmac<1>(A, Bop, acc, idx);
       else acc = smfmac<0>(A, Bop, acc, idx);
     }

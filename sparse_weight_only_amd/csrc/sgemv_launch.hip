@@ -17,7 +17,7 @@ namespace {
 
 // The descriptor must be one that sgemv_describe can produce.
 bool desc_consistent(const sgemv_desc* d) {
-  if (d->N < 1 || d->K < kChunkCols || d->K % kChunkCols || (d->nk != 1 && d->nk != 2)) return false;
+  if (d->N < 1 || d->K < kChunkCols || d->K % kChunkCols || !valid_nk(d->nk)) return false;
   const int32_t C = d->K / kChunkCols, T = (d->N + kBlockRows - 1) / kBlockRows;
   if (C > kMaxChunks || d->chunks != C || d->n_blocks != T || d->reserved != 0) return false;
   int64_t rows = 0, groups = 0;
@@ -30,7 +30,7 @@ bool desc_consistent(const sgemv_desc* d) {
   if (!valid_group(d->g_min, d->K) || !valid_group(d->g_max, d->K) || d->g_min > d->g_max) return false;
   if (d->class_rows[ilog2(d->g_min / 32)] == 0 || d->class_rows[ilog2(d->g_max / 32)] == 0) return false;
   if (d->kept != (int64_t)d->N * d->K * d->nk / 4) return false;
-  if (d->vals_bytes != d->kept / 2 || d->offs_bytes != d->kept / 4) return false;
+  if (d->vals_bytes != d->kept / 2 || d->offs_bytes != (d->nk == 4 ? 0 : d->kept / 4)) return false;
   const int64_t records = (int64_t)T * C * 64;
   if (d->off_codes != 0 || d->off_offs != align_up(records * piece_code_bytes(d->nk))) return false;
   if (d->off_perm != align_up(d->off_offs + records * piece_offs_bytes(d->nk))) return false;

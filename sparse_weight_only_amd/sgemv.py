@@ -161,12 +161,12 @@ def pack(w16: np.ndarray, nk: int, group_size) -> dict:
     gs = _host(np.asarray(group_size, dtype=np.int32), np.int32)
     if gs.shape != (N,):
         raise ValueError("group_size must have one entry per row")
-    if K % 256 or nk not in (1, 2):
+    if K % 256 or nk not in (1, 2, 4):
         _check(SGEMV_EINVAL, "sgemv_pack")
     kpr = K * nk // 4
     ng = int(np.sum(K // np.maximum(gs.astype(np.int64), 1)))
     vals = np.empty((N, kpr // 2), dtype=np.uint8)
-    offs = np.empty((N, kpr // 4), dtype=np.uint8)
+    offs = np.empty((N, 0 if nk == 4 else kpr // 4), dtype=np.uint8)   # dense (nk = 4): no offsets
     scale = np.empty(max(ng, 1), dtype=np.uint16)
     zero = np.empty(max(ng, 1), dtype=np.uint16)
     gptr = np.empty(N + 1, dtype=np.int32)

@@ -27,13 +27,13 @@ def grid_weights(N, K, nk, g, rng, s=2.0 ** -6):
     """Values k*s, k in [-8, 7], with every quantisation group keeping -8s and 7s."""
     W = rng.integers(-8, 8, (N, K)).astype(np.float64)
     for c0 in range(0, K, g):
-        W[:, c0: c0 + 4] = [-8, 7, 0, 0] if nk == 2 else [-8, 0, 0, 0]
+        W[:, c0: c0 + 4] = [-8, 7, 0, 0] if nk in (2, 4) else [-8, 0, 0, 0]
         if nk == 1:
             W[:, c0 + 4: c0 + 8] = [7, 0, 0, 0]
     return (W * s).astype(np.float16)
 
 
-@pytest.mark.parametrize("nk", [2, 1])
+@pytest.mark.parametrize("nk", [2, 1, 4])
 @pytest.mark.parametrize("N,K,gs_kind", [
     (1024, 1024, "u128"), (300, 4096, "mixed"), (77, 11008, "mixed"), (513, 2048, "all"),
     (40, 768, "mixed"), (1, 256, "u128"), (130, 1280, "all"), (96, 512, "u32"), (17, 32768, "all"),
@@ -159,7 +159,7 @@ def test_zero_input_gives_zero_output():
     assert np.all(y.view(np.uint16) == 0)
 
 
-@pytest.mark.parametrize("nk", [2, 1])
+@pytest.mark.parametrize("nk", [2, 1, 4])
 @pytest.mark.parametrize("N,K", [(16, 256), (600, 8192), (40, 11008), (17, 32768)])
 def test_every_launch_geometry(nk, N, K):
     """Shapes and batches that together launch every reachable kernel instance
@@ -201,7 +201,7 @@ def _run_group_checked(layers, Xs, B, guard=64):
     return out
 
 
-@pytest.mark.parametrize("nk", [2, 1])
+@pytest.mark.parametrize("nk", [2, 1, 4])
 def test_group_launch_exact_arithmetic(nk):
     """Several layers of different N and K in one launch: bit-exact on grid weights."""
     rng = np.random.default_rng(40 + nk)
@@ -284,3 +284,23 @@ def test_activation_aware_pruned_layer(nk):
     err = ogemv.normalized_error(y, ogemv.gemv(Wd, X), ogemv.abs_dot(Wd, X))
     say(f"  normalised error {err:.3e}")
     assert err <= TOL
+
+
+
+@pytest.mark.parametrize("L", [L for L in synth.cfg3() if L.nk == 2], ids=lambda L: L.name + "_dense")
+def test_dense_ablation_within_tolerance(L):
+    """Dense INT4 ablation (every element kept, same quantiser) of the MLP shapes."""
+    import dataclasses
+    Ld = dataclasses.replace(L, nk=4)
+    W = Ld.W()
+    gs = group_sizes(Ld, W)
+    say(f"case dense ablation {L.name}")
+    layer = make_layer(W, 4, gs)
+    check_pack_matches_oracle(W, 4, gs, layer.canon)
+    for B in (1, 4):
+        X = Ld.X(B)
+        y = run_checked(layer, X)
+        y_ref, D, _ = oracle_y(layer.canon, X)
+        err = ogemv.normalized_error(y, y_ref, D)
+        say(f"  B={B}: normalised error {err:.3e}")
+        assert err <= TOL

@@ -16,8 +16,11 @@ def decode_triplets(c):
         g = int(c["group_size"][n])
         for j in range(K * nk // 4):
             code = (int(c["vals"][n, j // 2]) >> (4 * (j % 2))) & 0xF
-            off = (int(c["offs"][n, j // 4]) >> (2 * (j % 4))) & 3
-            col = 4 * (j // nk) + off
+            if nk == 4:                          # dense ablation: element j is column j
+                col = j
+            else:
+                off = (int(c["offs"][n, j // 4]) >> (2 * (j % 4))) & 3
+                col = 4 * (j // nk) + off
             gi = int(c["gptr"][n]) + col // g
             s = float(np.uint16(c["scale"][gi]).view(np.float16))
             z = float(np.uint16(c["zero"][gi]).view(np.float16))
@@ -25,7 +28,7 @@ def decode_triplets(c):
     return out
 
 
-@pytest.mark.parametrize("nk", [1, 2])
+@pytest.mark.parametrize("nk", [1, 2, 4])
 def test_exact_rational_gemv(nk):
     rng = np.random.default_rng(10 + nk)
     N, K, B = 6, 256, 3

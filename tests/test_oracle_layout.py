@@ -13,6 +13,8 @@ def synthetic_canon(N, K, nk, gs, seed=0):
     q = rng.integers(0, 16, (N, kpr)).astype(np.uint8)
     o = rng.integers(0, 4, (N, kpr)).astype(np.uint8)
     vals, offs = pack.pack_bytes(q, o)
+    if nk == 4:
+        offs = np.zeros((N, 0), np.uint8)
     gs = np.asarray(gs, dtype=np.int32)
     gptr = np.zeros(N + 1, dtype=np.int64)
     gptr[1:] = np.cumsum(K // gs)
@@ -120,7 +122,7 @@ def test_records_follow_chunks_within_a_block():
 
 @pytest.mark.parametrize("N,K,nk", [
     (7, 256, 2), (16, 512, 2), (17, 768, 2), (33, 512, 1), (5, 1024, 1), (40, 256, 1),
-    (3, 2816, 2), (19, 2816, 1),
+    (3, 2816, 2), (19, 2816, 1), (7, 256, 4), (21, 1280, 4),
 ])
 def test_decode_inverts_build(N, K, nk):
     rng = np.random.default_rng(N * K + nk)
@@ -128,7 +130,7 @@ def test_decode_inverts_build(N, K, nk):
     canon, q, o = synthetic_canon(N, K, nk, gs, seed=N)
     L = layout.build(canon)
     q2, o2, szr, perm = layout.decode(L["blob"], N, K, nk, gs)
-    assert np.array_equal(q2, q) and np.array_equal(o2, o)
+    assert np.array_equal(q2, q) and (nk == 4 or np.array_equal(o2, o))
     sz = canon["scale"].astype(np.uint32) | (canon["zero"].astype(np.uint32) << 16)
     for n in range(N):
         assert np.array_equal(szr[n], sz[canon["gptr"][n]: canon["gptr"][n + 1]])
@@ -142,3 +144,29 @@ def test_decode_inverts_build(N, K, nk):
 def test_off14_positions_are_a_permutation():
     pos = [layout.off14_bit(m) for m in range(16)]
     assert sorted(pos) == list(range(0, 32, 2))
+
+
+def test_hand_placed_bytes_dense():
+    """Dense ablation (nk = 4): 64 elements per piece, no offset section."""
+    N, K, nk = 1, 256, 4
+    q = np.array([[j % 16 for j in range(K)]], dtype=np.uint8)
+    vals, _ = pack.pack_bytes(q, np.zeros((N, K), np.uint8))
+    canon = {"N": N, "K": K, "nk": nk, "group_size": np.array([256], np.int32), "vals": vals,
+             "offs": np.zeros((N, 0), np.uint8), "scale": np.array([0x3C00], np.uint16),
+             "zero": np.array([0x4800], np.uint16), "gptr": np.array([0, 1], np.int32)}
+    L = layout.build(canon)
+    off = L["offsets"]
+    # 64 lanes x 32 bytes of codes; the offset section is empty
+    assert (off["codes"], off["offs"], off["perm"], off["sz"], off["blob_bytes"]) == (0, 2048, 2048, 2304, 2560)
+    blob = L["blob"]
+    # lane 0, dword 0: positions 0 and 1 of the groups at columns 0-3, 4-7,
+    # 8-11, 12-15, i.e. elements 0,1,4,5,8,9,12,13 (codes equal), element k at
+    # nibble [0,4,1,5,2,6,3,7][k]: nibbles 0..7 hold 0,4,8,12,1,5,9,13
+    assert u32_at(blob, 0) == 0xD951C840
+    # dword 1: positions 2 and 3: elements 2,3,6,7,10,11,14,15 -> nibbles
+    # 2,6,10,14,3,7,11,15
+    assert u32_at(blob, 4) == 0xFB73EA62
+    # lane 16 (columns 64..127): dword 7 = columns 112..127, positions 2, 3:
+    # elements 114,115,118,119,122,123,126,127 -> codes 2,3,6,7,10,11,14,15
+    assert u32_at(blob, 16 * 32 + 28) == 0xFB73EA62
+    assert u32_at(blob, 2304) == 0x48003C00

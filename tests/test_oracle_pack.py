@@ -31,7 +31,7 @@ def test_hand_packed_rows_golden():
         assert c["rowptr"].tolist() == [0, 64 * nk]
 
 
-@pytest.mark.parametrize("nk", [1, 2])
+@pytest.mark.parametrize("nk", [1, 2, 4])
 def test_round_trip_and_sizes(nk):
     rng = np.random.default_rng(nk)
     N, K = 37, 512
@@ -40,12 +40,15 @@ def test_round_trip_and_sizes(nk):
     c = pack.pack_canonical(W, nk, gs)
     sz = pack.sizes(N, K, nk, gs)
     assert c["vals"].size == sz["vals_bytes"] == N * K * nk // 8
-    assert c["offs"].size == sz["offs_bytes"] == N * K * nk // 16
+    assert c["offs"].size == sz["offs_bytes"] == (0 if nk == 4 else N * K * nk // 16)
     assert c["scale"].size == c["zero"].size == sz["n_groups"] == int(np.sum(K // gs))
     assert c["gptr"][-1] == sz["n_groups"]
     q, o = pack.unpack_bytes(c["vals"], c["offs"])
     offs3, mask = prune.nm_prune(W, nk)
-    assert np.array_equal(o, offs3.reshape(N, -1))
+    if nk == 4:
+        assert mask.all() and np.array_equal(offs3.reshape(N, -1), np.tile(np.arange(4), (N, K // 4)))
+    else:
+        assert np.array_equal(o, offs3.reshape(N, -1))
     # re-quantising each group of the kept values gives the stored codes/scales
     kept = prune.kept_values(W, offs3)
     for n in range(N):

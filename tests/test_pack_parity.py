@@ -66,7 +66,8 @@ def test_decoder_set_sampled_layers():
         check_layer(L)
 
 
-@pytest.mark.parametrize("N,K,nk", [(200, 768, 2), (77, 1280, 1), (1, 256, 2), (15, 512, 1), (33, 11008, 2)])
+@pytest.mark.parametrize("N,K,nk", [(200, 768, 2), (77, 1280, 1), (1, 256, 2), (15, 512, 1), (33, 11008, 2),
+                                    (45, 1280, 4), (17, 11008, 4)])
 def test_ragged_blocks_and_mixed_classes(N, K, nk):
     """Partial last row block, row blocks that straddle two group sizes, every size."""
     rng = np.random.default_rng(N + K)
@@ -174,7 +175,7 @@ def test_launch_plan_covers_every_chunk_once(seed):
     and the LDS holds every wave's slice plus the partial sums."""
     rng = np.random.default_rng(seed)
     for _ in range(40):
-        nk = int(rng.choice([1, 2]))
+        nk = int(rng.choice([1, 2, 4]))
         K = 256 * int(rng.choice([1, 2, 3, 4, 5, 11, 16, 43, 64, 65, 128]))
         N = int(rng.integers(1, 12000))
         gs = rng.choice([32, 64, 128, 256], N).astype(np.int32)
@@ -341,3 +342,12 @@ def test_activation_aware_pruning_lowers_output_error_with_outlier_channels():
             Wp = oprune.pruned_dense(W, oprune.nm_prune_scored(W, nk, xc)[1]).astype(np.float64)
             errs[name] = np.linalg.norm(X.astype(np.float64) @ Wp.T - dense) / np.linalg.norm(dense)
         assert errs["activation_aware"] < errs["magnitude"], errs
+
+
+
+@pytest.mark.parametrize("L", [L for L in synth.cfg3() if L.nk == 2], ids=lambda L: L.name + "_dense")
+def test_dense_ablation_mlp_shapes(L):
+    """The dense INT4 ablation (nk = 4: every element kept, no offsets) of the
+    MLP shapes: groups, canonical arrays and blob bit-exact against the oracle."""
+    import dataclasses
+    check_layer(dataclasses.replace(L, nk=4, name=L.name.replace("2of4", "dense")))
