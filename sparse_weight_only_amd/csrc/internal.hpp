@@ -92,9 +92,10 @@ inline Launch launch_geometry(int C, int T, int B) {
   L.imax = bucket(cpw);
   // x of phase chunks staged at once: B * phase <= 16 keeps the staging at
   // most 8 16-byte loads per lane
+  // (a power of two: the kernel splits x units with a shift)
   int ph = 1;
   while (ph * 2 <= cpw && B * ph * 2 <= 16) ph *= 2;
-  if (ph < cpw && B * cpw <= 16) ph = cpw;
+  if (ph < cpw && B * cpw <= 16 && (cpw & (cpw - 1)) == 0) ph = cpw;
   L.phase = ph;
   L.xloads = (B * ph * 32 + 63) / 64;
   L.xmax = bucket(L.xloads);

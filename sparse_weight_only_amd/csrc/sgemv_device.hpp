@@ -149,7 +149,10 @@ template <int NK, int IMAX, int XMAX>
 __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int CB = 8 * NK, OB = 4 * NK;   // bytes of one piece's codes and offsets
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, W = blockDim.x >> 6;
+  // the wave index is the same on every lane: keep it (and what follows
+  // from it) in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int W = blockDim.x >> 6;
   const int r = lane & 15, q = lane >> 4;
   const int B = p.B, PH = p.phase;
   const auto rbuf = make_rsrc(p.blob, p.blob_bytes);
@@ -164,21 +167,28 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
   const int glog = 5 + cls;
   const int wb0 = words_before(p, rb * 16);
   const uint32_t rec_words = (uint32_t)(words_before(p, rb * 16 + 16) - wb0);
-  const uint32_t sz_lane = (uint32_t)(words_before(p, row) - wb0) + (uint32_t)((64 * q) >> glog);
+  // a block whose 16 rows share one group size (all but at most three blocks
+  // of a layer) holds 256/g words per row, row after row
+  const int cls_first = (rb * 16 >= p.cls_row[1]) + (rb * 16 >= p.cls_row[2]) + (rb * 16 >= p.cls_row[3]);
+  const bool one_class = rec_words == (uint32_t)(16 * (8 >> cls_first));
+  const uint32_t sz_row = one_class ? (uint32_t)(r * (8 >> cls_first)) : (uint32_t)(words_before(p, row) - wb0);
+  const uint32_t sz_lane = sz_row + (uint32_t)((64 * q) >> glog);
   const uint32_t sz_block = (uint32_t)wb0 * (uint32_t)p.C;
   const bool g32 = cls == 0;
 
   // 0. original index of row tid % 16 of the block, for the lanes that write y
   const uint32_t orow = bload1<kCached>(rbuf, p.off_perm + (uint32_t)(rb * 16 + (tid & 15)) * 4u);
 
-  // 1. x slice of the first phase: B rows x (PH * 256) columns, 16 bytes per load
+  // 1. x slice of the first phase: B rows x (PH * 256) columns, 16 bytes per
+  // load; PH is a power of two, so a unit's row and column are a shift and a mask
   const int span16 = PH * 32;
+  const int span_log = 5 + (31 - __builtin_clz((unsigned)PH));
   u32x4 xv[XMAX];
   auto issue_x = [&](int first) {   // chunks c0 + first .. c0 + first + PH - 1
     const int lim = (ncw - first < PH ? ncw - first : PH) * 32;
 #pragma unroll
     for (int j = 0; j < XMAX; ++j) {
-      const int u = lane + 64 * j, b = u / span16, cu = u - b * span16;
+      const int u = lane + 64 * j, b = u >> span_log, cu = u & (span16 - 1);
       const bool ok = b < B && cu < lim;
       xv[j] = bload4<kCached>(rx, ok ? (uint32_t)(b * p.K + (c0 + first) * 256 + cu * 8) * 2u : kOutOfRange);
     }
@@ -217,6 +227,12 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
 
   _Float16* xs = reinterpret_cast<_Float16*>(smem) + w * (B * span16 * 8);
   float* part = reinterpret_cast<float*>(smem + W * B * span16 * 16);
+  // small batches: the slots of waves this workgroup does not have hold +0,
+  // so that the final sum reads all 16 slots without a test per slot (the
+  // sum is then on the critical path of few lanes, and short)
+  if (B <= 4)
+    for (int e = tid; e < 16 * B * 16; e += blockDim.x)   // (batch row, row, slot)
+      if ((e & 15) >= W) part[e] = 0.f;
   const uint32_t magic = opaque_vgpr(0x64006400u);
   const int bcol = (lane & 15) < B ? (lane & 15) : 0;
   const _Float16* xrow = xs + bcol * (span16 * 8) + 64 * (q >> 1) + 8 * (q & 1);
@@ -311,9 +327,14 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
     const float vv[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
                           v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
     float s = 0.f;
+    if (B <= 4) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      if (v < W) s += vv[v];
+      for (int v = 0; v < 16; ++v) s += vv[v];   // slots W.. hold +0
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (v < W) s += vv[v];
+    }
     const int n = (int)orow;
     if (n >= 0 && n < p.N) p.y[(int64_t)b * p.N + n] = __builtin_bit_cast(uint16_t, (_Float16)s);
   }

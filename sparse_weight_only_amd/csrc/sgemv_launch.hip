@@ -46,7 +46,7 @@ int make_plan(const sgemv_desc* d, int32_t B, sgemv_plan_t* pl, Launch* geo) {
   if (!desc_consistent(d)) return SGEMV_ESIZE;
   const Launch L = launch_geometry(d->chunks, d->n_blocks, B);
   if (L.waves < 1 || L.waves > kMaxWaves || L.cpw > kMaxChunksPerWave || L.xloads > 8) return SGEMV_ESIZE;
-  if (L.lds > 160 * 1024) return SGEMV_ESIZE;
+  if (L.lds > 160 * 1024 || (L.phase & (L.phase - 1)) != 0) return SGEMV_ESIZE;
   sgemv_plan_t q;
   memset(&q, 0, sizeof q);
   q.grid = d->n_blocks;
@@ -103,7 +103,7 @@ int make_group_plan(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_pla
   if (blocks > ((int64_t)1 << 30)) return SGEMV_ESIZE;
   const Launch L = launch_geometry(cmax, (int32_t)blocks, B);
   if (L.waves < 1 || L.waves > kMaxWaves || L.cpw > kMaxChunksPerWave || L.xloads > 8) return SGEMV_ESIZE;
-  if (L.lds > 160 * 1024) return SGEMV_ESIZE;
+  if (L.lds > 160 * 1024 || (L.phase & (L.phase - 1)) != 0) return SGEMV_ESIZE;
   sgemv_plan_t q;
   memset(&q, 0, sizeof q);
   q.grid = blocks;

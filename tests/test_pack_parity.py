@@ -188,6 +188,7 @@ def test_launch_plan_covers_every_chunk_once(seed):
             assert 1 <= pl.chunks_per_wave <= 8
             assert (pl.waves - 1) * pl.chunks_per_wave < C <= pl.waves * pl.chunks_per_wave
             assert 1 <= pl.phase_chunks <= pl.chunks_per_wave
+            assert pl.phase_chunks & (pl.phase_chunks - 1) == 0          # a power of two
             assert pl.x_loads == -(-(B * pl.phase_chunks * 32) // 64) and pl.x_loads <= 8
             assert pl.lds_bytes == pl.waves * B * pl.phase_chunks * 512 + B * 16 * 16 * 4
             assert pl.lds_bytes <= 160 * 1024
