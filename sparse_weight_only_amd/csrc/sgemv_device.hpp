@@ -73,17 +73,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 // CPOL: 0 = default caching, 2 = non-temporal (the weights are read once).
 constexpr int kCached = 0, kStream = 2;
+// soff is a wave-uniform offset added to every lane's: kOutOfRange there turns
+// off the whole load for the wave (offset + 2^31 stays below 2^32 and beyond
+// any buffer here) without a per-lane select.
 template <int CPOL>
-__device__ __forceinline__ u32x4 bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL));
+__device__ __forceinline__ u32x4 bload4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, CPOL));
 }
 template <int CPOL>
-__device__ __forceinline__ u32x2 bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CPOL));
+__device__ __forceinline__ u32x2 bload2(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, CPOL));
 }
 template <int CPOL>
-__device__ __forceinline__ uint32_t bload1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CPOL);
+__device__ __forceinline__ uint32_t bload1(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, CPOL);
 }
 
 // A VGPR holding c whose value the compiler cannot see, so that (a & m) | c
@@ -162,7 +165,6 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
 
   // this lane's sorted row, its group size 32 << cls and its scale|zero words
   const int row = rb * 16 + r;
-  const bool row_ok = row < p.N;
   const int cls = (row >= p.cls_row[1]) + (row >= p.cls_row[2]) + (row >= p.cls_row[3]);
   const int glog = 5 + cls;
   const int wb0 = words_before(p, rb * 16);
@@ -190,7 +192,8 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
     for (int j = 0; j < XMAX; ++j) {
       const int u = lane + 64 * j, b = u >> span_log, cu = u & (span16 - 1);
       const bool ok = b < B && cu < lim;
-      xv[j] = bload4<kCached>(rx, ok ? (uint32_t)(b * p.K + (c0 + first) * 256 + cu * 8) * 2u : kOutOfRange);
+      xv[j] = bload4<kCached>(rx, ok ? (__umul24((uint32_t)b, (uint32_t)p.K) + (uint32_t)((c0 + first) * 256 + cu * 8)) * 2u
+                                     : kOutOfRange);
     }
   };
   issue_x(0);
@@ -205,23 +208,25 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
 #pragma unroll
   for (int i = 0; i < IMAX; ++i) {
     const int c = c0 + i;
-    const bool ok = i < ncw;
+    const uint32_t off = i < ncw ? 0u : kOutOfRange;   // wave-uniform: chunk c exists
     const uint32_t rec = (uint32_t)(rb * p.C + c) * 64u + lane;
+    // scale|zero: padding rows of a last, partial block read whatever words
+    // follow (or zeros past the blob); their sums are never stored
     const uint32_t so = p.off_sz + (sz_block + (uint32_t)c * rec_words + sz_lane) * 4u;
     if constexpr (NK == 4) {
       // dense ablation: 32 bytes of codes, no offsets
-      const u32x4 lo = bload4<kStream>(rbuf, ok ? p.off_codes + rec * CB : kOutOfRange);
-      const u32x4 hi = bload4<kStream>(rbuf, ok ? p.off_codes + rec * CB + 16u : kOutOfRange);
+      const u32x4 lo = bload4<kStream>(rbuf, p.off_codes + rec * CB, off);
+      const u32x4 hi = bload4<kStream>(rbuf, p.off_codes + rec * CB + 16u, off);
       cv[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       ov[i] = 0u;
     } else if constexpr (NK == 2) {
-      cv[i] = bload4<kStream>(rbuf, ok ? p.off_codes + rec * CB : kOutOfRange);
-      ov[i] = bload2<kStream>(rbuf, ok ? p.off_offs + rec * OB : kOutOfRange);
+      cv[i] = bload4<kStream>(rbuf, p.off_codes + rec * CB, off);
+      ov[i] = bload2<kStream>(rbuf, p.off_offs + rec * OB, off);
     } else {
-      cv[i] = bload2<kStream>(rbuf, ok ? p.off_codes + rec * CB : kOutOfRange);
-      ov[i] = bload1<kStream>(rbuf, ok ? p.off_offs + rec * OB : kOutOfRange);
+      cv[i] = bload2<kStream>(rbuf, p.off_codes + rec * CB, off);
+      ov[i] = bload1<kStream>(rbuf, p.off_offs + rec * OB, off);
     }
-    sv[i] = bload2<kStream>(rbuf, ok && row_ok ? so : kOutOfRange);
+    sv[i] = bload2<kStream>(rbuf, so, off);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -235,7 +240,7 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
       if ((e & 15) >= W) part[e] = 0.f;
   const uint32_t magic = opaque_vgpr(0x64006400u);
   const int bcol = (lane & 15) < B ? (lane & 15) : 0;
-  const _Float16* xrow = xs + bcol * (span16 * 8) + 64 * (q >> 1) + 8 * (q & 1);
+  const _Float16* xrow = xs + __umul24((uint32_t)bcol, (uint32_t)(span16 * 8)) + 64 * (q >> 1) + 8 * (q & 1);
   f4 acc = {0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
@@ -336,7 +341,8 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
         if (v < W) s += vv[v];
     }
     const int n = (int)orow;
-    if (n >= 0 && n < p.N) p.y[(int64_t)b * p.N + n] = __builtin_bit_cast(uint16_t, (_Float16)s);
+    // B * N < 2^31 (the blob size bounds N), so 32-bit indexing is enough
+    if (n >= 0 && n < p.N) p.y[(uint32_t)(b * p.N + n)] = __builtin_bit_cast(uint16_t, (_Float16)s);
   }
 }
 
