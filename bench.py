@@ -23,7 +23,8 @@ Timing protocol
 Beside the step, the same line reports
 * ``ablation``: the up and down MLP weights as a dense INT4 layer (every
   element kept, same quantiser: the plain weight-only GEMV that SparseGemv
-  extends) and as a plain FP16 GEMV through torch (hipBLASLt, launched
+  extends), in the FP16-valued 2bit-CSR form (N:M sparsity without INT4) at
+  2:4 and 1:4, and as a plain FP16 GEMV through torch (hipBLASLt, launched
   eagerly: a library call stays out of graph capture), at B = 1, cold, with
   the sparse layers' speedups;
 * ``beam``: µs and GB/s per call of the beam-batch shapes (up and down of
@@ -333,10 +334,23 @@ def main():
             base = L.name.replace("_2of4", "")
             s24 = per_layer[base + "_2of4"]["us_per_call"]
             s14 = per_layer[base + "_1of4"]["us_per_call"]
+            # the FP16-valued form (N:M sparsity without INT4) at both N:M choices
+            f16 = {}
+            for nk in (2, 1):
+                d16 = sg.describe_fp16(Ld.N, Ld.K, nk)
+                h16 = torch.from_numpy(sg.layout_fp16(d16, sg.pack_fp16(W, nk)))
+                R = max(2, -(-COLD_BYTES // d16.blob_bytes))
+                copies = [h16.to(dev) for _ in range(R)]
+                us_f = per_call_us(d16, copies, x, y, 1, args.layer_calls)
+                nb_f = sg.algorithmic_bytes(d16, 1)
+                f16["2of4" if nk == 2 else "1of4"] = {"us_per_call": round(us_f, 3), "bytes": nb_f,
+                                                      "GBps": round(nb_f / (us_f * 1e-6) / 1e9, 1)}
+                del copies
             ablation[base] = {
                 "dense_int4": {"us_per_call": round(us_d, 3), "bytes": nb_d, "GBps": round(nb_d / (us_d * 1e-6) / 1e9, 1)},
                 "fp16_torch_linear": {"us_per_call": round(us_h, 3), "bytes": nb_h,
                                       "GBps": round(nb_h / (us_h * 1e-6) / 1e9, 1)},
+                "fp16_values_2bitcsr": f16,
                 "speedup_2of4_vs_dense_int4": round(us_d / s24, 3),
                 "speedup_1of4_vs_dense_int4": round(us_d / s14, 3),
                 "speedup_2of4_vs_fp16": round(us_h / s24, 3),

@@ -49,9 +49,9 @@ typedef struct sgemv_desc {
   int32_t chunks;        /* column chunks of 256 dense columns per row: K / 256        */
   int32_t g_min, g_max;  /* smallest and largest group size present                    */
   int32_t class_rows[4]; /* rows with group size 32, 64, 128, 256 (sorted in that order) */
-  int32_t reserved;      /* zero                                                       */
+  int32_t value_format;  /* 0: INT4 codes with group scale/zero; 1: FP16 values       */
   int64_t kept;          /* N*K*nk/4 kept elements                                     */
-  int64_t vals_bytes;    /* canonical code array: kept/2 bytes (one nibble each)       */
+  int64_t vals_bytes;    /* canonical value array: kept/2 bytes (INT4), kept*2 (FP16)  */
   int64_t offs_bytes;    /* canonical offset array: kept/4 bytes (2 bits each); 0 dense */
   int64_t n_groups;      /* sum_n K/g_n: one FP16 scale and one FP16 zero each         */
   int64_t off_codes;     /* byte offsets of the blob sections (256-byte aligned)       */
@@ -76,6 +76,18 @@ typedef struct sgemv_desc {
  * Errors: EINVAL for bad arguments, ESIZE beyond the supported sizes. */
 int sgemv_describe(int32_t N, int32_t K, int32_t nk, const int32_t* group_size,
                    sgemv_desc* out);
+
+/* sgemv_describe_fp16 - descriptor of the FP16-valued form: the same N:M
+ * selection and 2-bit offsets, each kept value stored as FP16 (no groups, no
+ * scale or zero): the semi-structured layer-wise FP16 mixed sparsity of P1 §1
+ * ("our core idea") before INT4 compression.
+ *   N, K, nk : as sgemv_describe (nk 1 or 2).
+ * The descriptor has value_format 1, n_groups 0, no class rows, and its blob
+ * holds values [blocks][chunks][64 lanes][32*nk bytes] (each lane's 16*nk
+ * kept values in element order), offsets as the INT4 form, and perm (the
+ * identity: there are no group sizes to sort by).
+ * Errors: EINVAL, ESIZE as sgemv_describe. */
+int sgemv_describe_fp16(int32_t N, int32_t K, int32_t nk, sgemv_desc* out);
 
 /* sgemv_select_groups - adaptive group size per output channel (P1 §3.2
  * "Adaptive group quantization"; sensitivity from the first term of eq. (3)).
@@ -129,6 +141,18 @@ int sgemv_pack(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
                const int32_t* group_size, uint8_t* vals, uint8_t* offs,
                uint16_t* scale, uint16_t* zero, int32_t* gptr, int32_t* rowptr);
 
+/* sgemv_pack_fp16 - dense FP16 W -> N:M prune (as sgemv_pack) -> FP16-valued
+ * 2bit-CSR: vals16 [N][K*nk/4] FP16 bits of kept element j (ascending column),
+ * offs [N][K*nk/16] as sgemv_pack, rowptr [N+1] = n*K*nk/4 (host arrays).
+ * Errors: EINVAL (shape, nk not 1 or 2, NULL, non-finite weight). */
+int sgemv_pack_fp16(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
+                    uint16_t* vals16, uint8_t* offs, int32_t* rowptr);
+
+/* sgemv_layout_fp16 - FP16-valued canonical arrays -> kernel-layout blob
+ * (host buffer of d->blob_bytes, fully written); d from sgemv_describe_fp16.
+ * Errors: EINVAL (NULL, a descriptor of the other format), ESIZE. */
+int sgemv_layout_fp16(const sgemv_desc* d, const uint16_t* vals16, const uint8_t* offs, void* blob);
+
 /* sgemv_layout - canonical arrays -> kernel-layout blob (host). The blob holds
  * the same bits reordered for the matrix-core kernel (no duplication; zero
  * padding only for the rows of a last, partial row block):
@@ -166,7 +190,8 @@ int sgemv_layout(const sgemv_desc* d, const uint8_t* vals, const uint8_t* offs,
  * Numerics: each weight enters as FP16 (code - zero) * scale (one rounding,
  * relative error <= 2^-11), products and sums in FP32, y rounded to FP16;
  * |y - W'x| <= (2^-11 + n 2^-24) sum_k |W'[n][k] x[k]| + 2^-11 |y| for n
- * kept elements per row. Non-finite x gives non-finite rows, as the dense
+ * kept elements per row (FP16-valued layers: the weights enter exactly, and
+ * the first term drops to n 2^-24). Both value formats are accepted. Non-finite x gives non-finite rows, as the dense
  * product does.
  * Enqueues one kernel and returns without synchronising. x and y must not
  * overlap the blob or each other. Deterministic: the same inputs give the
@@ -208,7 +233,7 @@ typedef struct sgemv_task {
  * one launch per GEMV pays the dispatch, ramp-up and drain of a kernel each
  * time, which a 4096 x 4096 layer's few megabytes cannot hide).
  *   tasks      : host array of count layers; every layer has the same nk
- *                (EINVAL otherwise); N and K may differ (workgroups of a
+ *                and value format (EINVAL otherwise); N and K may differ (workgroups of a
  *                layer with fewer column chunks than the widest one leave
  *                waves idle, so grouping layers of equal K is best).
  *   count      : 1..SGEMV_MAX_GROUP.

@@ -11,8 +11,17 @@ from .pack import unpack_bytes
 
 
 def dequant_dense(canon: dict) -> np.ndarray:
-    """Canonical arrays -> dense W' (FP64 [N, K], zeros at pruned positions)."""
+    """Canonical arrays -> dense W' (FP64 [N, K], zeros at pruned positions).
+    FP16-valued arrays (key ``vals16``) hold the kept values themselves."""
     N, K, nk = canon["N"], canon["K"], canon["nk"]
+    if "vals16" in canon:
+        _, o = unpack_bytes(np.zeros((N, 1), np.uint8), canon["offs"])
+        kpr = K * nk // 4
+        j = np.arange(kpr, dtype=np.int64)
+        col = 4 * (j[None, :] // nk) + o.astype(np.int64)
+        Wd = np.zeros((N, K), dtype=np.float64)
+        np.put_along_axis(Wd, col, from_bits(canon["vals16"]), axis=1)
+        return Wd
     gs = np.asarray(canon["group_size"], dtype=np.int64)
     q, o = unpack_bytes(canon["vals"], canon["offs"])
     if nk == 4:                                   # dense: no stored offsets

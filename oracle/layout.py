@@ -33,7 +33,9 @@ holds, for the 4 groups of columns 16t .. 16t + 15 of the piece, the
 elements at in-group positions 2h and 2h + 1: dword element k = 2g + p'
 (group g, position 2h + p') at nibble NIB[2][k], so that each dword is a
 2-of-4 operand whose index field is the constant (0, 1) or (2, 3) per
-group. The offset section is empty.
+group. A record stores the pieces' dwords 0-3 for all 64 lanes, then dwords
+4-7 (16-byte slices, so that one load instruction reads 1 KiB
+contiguously). The offset section is empty.
 
 Scale/zero: one 32-bit word per group, FP16 scale in the low half, FP16 zero
 in the high half; records (b, c) in (b, c) order, each listing the rows of
@@ -132,6 +134,9 @@ def build(canon: dict) -> dict:
     owp = np.zeros((T * 16,) + ow.shape[1:], dtype=np.uint32)
     cwp[:N], owp[:N] = cw, ow
     codes = cwp.reshape(T, 16, C, 4, -1).transpose(0, 2, 3, 1, 4)     # [T, C, q, r, dw]
+    if nk == 4:
+        # 16-byte slices: slice h of every lane, then slice h + 1
+        codes = codes.reshape(T, C, 64, 2, 4).transpose(0, 1, 3, 2, 4)   # [T, C, h, lane, 4 dwords]
     offs = owp.reshape(T, 16, C, 4, -1).transpose(0, 2, 3, 1, 4)
     # scale/zero records
     sz_words = []
@@ -172,6 +177,8 @@ def decode(blob: np.ndarray, N: int, K: int, nk: int, group_size):
     u32 = lambda at, n: np.frombuffer(blob[at: at + 4 * n].tobytes(), dtype="<u4")
     perm = np.frombuffer(blob[off["perm"]: off["perm"] + 64 * T].tobytes(), dtype="<i4")
     cw = u32(off["codes"], T * C * 64 * 2 * nk).reshape(T, C, 64, 2 * nk)
+    if nk == 4:
+        cw = cw.reshape(T, C, 2, 64, 4).transpose(0, 1, 3, 2, 4).reshape(T, C, 64, 8)
     now = piece_offs_bytes(nk) // 4
     ow = u32(off["offs"], T * C * 64 * now).reshape(T, C, 64, now)
     szw = u32(off["sz"], n_groups)
@@ -209,3 +216,89 @@ def decode(blob: np.ndarray, N: int, K: int, nk: int, group_size):
                 at += per
     assert at == n_groups
     return q, o, sz_rows, perm[:N]
+
+
+# ---- FP16-valued form (no groups): values in place of codes, no scale/zero
+
+def section_offsets16(N: int, K: int, nk: int) -> dict:
+    """Sections of the FP16-valued blob: values, offsets as in the INT4 form,
+    perm; no scale/zero words. A lane's piece holds its 16*nk kept values
+    (FP16, element order) in 2*nk 16-byte slices; record (b, c) stores slice
+    0 of all 64 lanes, then slice 1, and so on."""
+    T, C = -(-N // 16), K // 256
+    records = T * C * 64
+    off = {"values": 0}
+    off["offs"] = _align(records * 32 * nk)
+    off["perm"] = _align(off["offs"] + records * 4 * nk)
+    off["blob_bytes"] = _align(off["perm"] + 4 * 16 * T)
+    return off
+
+
+def _piece_offsets(o_sorted: np.ndarray, N: int, C: int, nk: int) -> np.ndarray:
+    """Offset words [N, C, 4, nk] of every piece (same rules as the INT4 form)."""
+    kpp = 16 * nk
+    os_ = o_sorted.astype(np.uint32).reshape(N, C, 4, kpp)
+    if nk == 2:
+        od = os_.reshape(N, C, 4, 2, 16)
+        ow = np.zeros((N, C, 4, 2), dtype=np.uint32)
+        for m in range(16):
+            ow |= od[..., m] << np.uint32(2 * m)
+    else:
+        ow = np.zeros((N, C, 4, 1), dtype=np.uint32)
+        for m in range(16):
+            ow[..., 0] |= os_[..., m] << np.uint32(off14_bit(m))
+    return ow
+
+
+def build16(canon16: dict) -> dict:
+    """FP16-valued canonical arrays -> kernel blob (rows in index order: with
+    no group sizes there is nothing to sort by, perm is the identity)."""
+    N, K, nk = canon16["N"], canon16["K"], canon16["nk"]
+    T, C, kpp = -(-N // 16), K // 256, 16 * nk
+    v16 = np.asarray(canon16["vals16"], dtype=np.uint16)
+    _, o = unpack_bytes(np.zeros((N, 1), np.uint8), canon16["offs"])
+    vals = np.zeros((T * 16, C, 4, kpp), dtype=np.uint16)
+    vals[:N] = v16.reshape(N, C, 4, kpp)
+    ow = np.zeros((T * 16, C, 4, nk), dtype=np.uint32)
+    ow[:N] = _piece_offsets(o, N, C, nk)
+    values = vals.reshape(T, 16, C, 4, kpp).transpose(0, 2, 3, 1, 4)      # [T, C, q, r, kpp]
+    # 16-byte slices (8 values): slice k of all 64 lanes, then slice k + 1
+    values = values.reshape(T, C, 64, 2 * nk, 8).transpose(0, 1, 3, 2, 4)  # [T, C, k, lane, 8]
+    offs = ow.reshape(T, 16, C, 4, nk).transpose(0, 2, 3, 1, 4)
+    perm = np.full(16 * T, -1, dtype=np.int32)
+    perm[:N] = np.arange(N, dtype=np.int32)
+    off = section_offsets16(N, K, nk)
+    blob = np.zeros(off["blob_bytes"], dtype=np.uint8)
+    raw = np.ascontiguousarray(values).astype("<u2").view(np.uint8).reshape(-1)
+    blob[off["values"]: off["values"] + raw.size] = raw
+    raw = np.ascontiguousarray(offs).astype("<u4").view(np.uint8).reshape(-1)
+    blob[off["offs"]: off["offs"] + raw.size] = raw
+    raw = perm.astype("<i4").view(np.uint8)
+    blob[off["perm"]: off["perm"] + raw.size] = raw
+    return {"blob": blob, "offsets": off, "perm": perm}
+
+
+def decode16(blob: np.ndarray, N: int, K: int, nk: int):
+    """Inverse of build16: FP16 bits [N, K*nk/4] and offsets [N, K*nk/4]."""
+    T, C, kpp = -(-N // 16), K // 256, 16 * nk
+    off = section_offsets16(N, K, nk)
+    v = np.frombuffer(blob[off["values"]: off["values"] + T * C * 64 * kpp * 2].tobytes(), dtype="<u2")
+    v = v.reshape(T, C, 2 * nk, 64, 8).transpose(0, 1, 3, 2, 4).reshape(T, C, 4, 16, kpp)
+    ow = np.frombuffer(blob[off["offs"]: off["offs"] + T * C * 64 * 4 * nk].tobytes(), dtype="<u4")
+    ow = ow.reshape(T, C, 4, 16, nk)
+    kpr = K * nk // 4
+    q16 = np.zeros((N, kpr), dtype=np.uint16)
+    o = np.zeros((N, kpr), dtype=np.uint8)
+    for n in range(N):
+        b, r = divmod(n, 16)
+        for c in range(C):
+            for qq in range(4):
+                e0 = kpp * (4 * c + qq)
+                q16[n, e0: e0 + kpp] = v[b, c, qq, r]
+                for m in range(kpp):
+                    if nk == 2:
+                        word, bit = divmod(m, 16)
+                        o[n, e0 + m] = (ow[b, c, qq, r, word] >> (2 * bit)) & 3
+                    else:
+                        o[n, e0 + m] = (ow[b, c, qq, r, 0] >> off14_bit(m)) & 3
+    return q16, o

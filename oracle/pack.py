@@ -105,3 +105,24 @@ def pack_canonical(W16: np.ndarray, nk: int, group_size) -> dict:
         "rowptr": (np.arange(N + 1, dtype=np.int64) * kpr).astype(np.int32),
         "mask": mask,
     }
+
+
+def pack_fp16_canonical(W16: np.ndarray, nk: int) -> dict:
+    """FP16-valued 2bit-CSR (P1 §1 "our core idea" and contributions, first
+    item: semi-structured layer-wise FP16 mixed sparsity, before INT4): the
+    same N:M selection and 2-bit offsets, the kept values stored as FP16.
+
+    * vals16 uint16 [N, K*nk/4]  FP16 bits of kept element j (ascending column);
+    * offs   uint8  [N, K*nk/16] as in the INT4 form;
+    * rowptr int32  [N+1]        n*K*nk/4.
+    """
+    W = np.asarray(W16, dtype=np.float16)
+    N, K = W.shape
+    if K % 256 or nk not in (1, 2):
+        raise ValueError("K must be a multiple of 256 and nk in {1, 2}")
+    offs3, mask = _prune.nm_prune(W, nk)
+    kept16 = _prune.kept_values(W, offs3)
+    _, offs = pack_bytes(np.zeros(kept16.shape, np.uint8), offs3.reshape(N, -1))
+    kpr = K * nk // 4
+    return {"N": N, "K": K, "nk": nk, "vals16": bits(kept16), "offs": offs,
+            "rowptr": (np.arange(N + 1, dtype=np.int64) * kpr).astype(np.int32), "mask": mask}

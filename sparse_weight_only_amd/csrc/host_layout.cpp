@@ -18,7 +18,8 @@
 //    16*((m/4)%2) + (m/4 < 2 ? [0,4,10,14] : [2,6,8,12])[m%4];
 //  - dense ablation (nk = 4, no offsets): code dword 2t + h holds positions
 //    2h and 2h + 1 of the 4 groups of piece columns 16t .. 16t + 15, element
-//    k = 2g + p at nibble [0,4,1,5,2,6,3,7][k];
+//    k = 2g + p at nibble [0,4,1,5,2,6,3,7][k]; a record stores dwords 0-3 of
+//    all 64 lanes, then dwords 4-7 (so one load reads 1 KiB contiguously);
 //  - perm: original row of each sorted row, -1 for padding rows;
 //  - scale|zero<<16 words: records (b, c) in order, each the rows of block b
 //    in order, each with its 256/g words of chunk c (groups c*256/g ..).
@@ -86,6 +87,72 @@ extern "C" int sgemv_describe(int32_t N, int32_t K, int32_t nk, const int32_t* g
   d.blob_bytes = align_up(d.off_sz + 4 * n_groups + 8);
   if (d.blob_bytes >= ((int64_t)1 << 31)) return SGEMV_ESIZE;
   *out = d;
+  return SGEMV_OK;
+}
+
+extern "C" int sgemv_describe_fp16(int32_t N, int32_t K, int32_t nk, sgemv_desc* out) {
+  if (!out) return SGEMV_EINVAL;
+  if (N < 1 || K < kChunkCols || K % kChunkCols != 0 || (nk != 1 && nk != 2)) return SGEMV_EINVAL;
+  if (K / kChunkCols > kMaxChunks) return SGEMV_ESIZE;
+  sgemv_desc d;
+  memset(&d, 0, sizeof d);
+  const int32_t T = (N + kBlockRows - 1) / kBlockRows, C = K / kChunkCols;
+  d.N = N; d.K = K; d.nk = nk;
+  d.n_blocks = T;
+  d.chunks = C;
+  d.value_format = 1;
+  d.kept = (int64_t)N * K * nk / 4;
+  d.vals_bytes = d.kept * 2;
+  d.offs_bytes = d.kept / 4;
+  const int64_t records = (int64_t)T * C * 64;
+  d.off_codes = 0;
+  d.off_offs = align_up(records * piece_value16_bytes(nk));
+  d.off_perm = align_up(d.off_offs + records * piece_offs_bytes(nk));
+  d.off_sz = align_up(d.off_perm + 4 * (int64_t)T * kBlockRows);   // no words: the blob ends here
+  d.blob_bytes = d.off_sz;
+  if (d.blob_bytes >= ((int64_t)1 << 31)) return SGEMV_ESIZE;
+  *out = d;
+  return SGEMV_OK;
+}
+
+extern "C" int sgemv_layout_fp16(const sgemv_desc* d, const uint16_t* vals16, const uint8_t* offs, void* blob_v) {
+  if (!d || !vals16 || !offs || !blob_v || d->value_format != 1) return SGEMV_EINVAL;
+  sgemv_desc chk;
+  const int rc = sgemv_describe_fp16(d->N, d->K, d->nk, &chk);
+  if (rc) return rc;
+  if (memcmp(&chk, d, sizeof chk) != 0) return SGEMV_ESIZE;
+  const int32_t N = d->N, K = d->K, nk = d->nk, T = d->n_blocks, C = d->chunks, kpr = K * nk / 4;
+  const int kpp = 16 * nk, pvb = piece_value16_bytes(nk), pob = piece_offs_bytes(nk);
+  uint8_t* blob = (uint8_t*)blob_v;
+  memset(blob, 0, (size_t)d->blob_bytes);
+  int32_t* pm = (int32_t*)(blob + d->off_perm);
+  for (int32_t i = 0; i < T * kBlockRows; ++i) pm[i] = i < N ? i : -1;
+  for (int32_t n = 0; n < N; ++n) {
+    const int32_t b = n / kBlockRows, r = n % kBlockRows;
+    const uint16_t* vrow = vals16 + (int64_t)n * kpr;
+    const uint8_t* orow = offs + (int64_t)n * (kpr / 4);
+    for (int32_t c = 0; c < C; ++c)
+      for (int q = 0; q < 4; ++q) {
+        const int64_t rec = ((int64_t)b * C + c) * 64 + r + 16 * q;
+        const int64_t e0 = (int64_t)kpp * (4 * c + q);
+        // values in element order, in 16-byte slices: slice k of all 64 lanes, then slice k + 1
+        const int64_t rec0 = ((int64_t)b * C + c) * 64;
+        for (int k = 0; k < pvb / 16; ++k)
+          memcpy(blob + d->off_codes + rec0 * pvb + (k * 64 + r + 16 * q) * 16, vrow + e0 + 8 * k, 16);
+        if (nk == 2) {
+          memcpy(blob + d->off_offs + rec * pob, orow + e0 / 4, pob);
+        } else {
+          uint32_t word = 0;
+          for (int m = 0; m < 16; ++m) {
+            const int64_t j = e0 + m;
+            const uint32_t o = (orow[j >> 2] >> (2 * (j & 3))) & 3u;
+            const int t = m / 4, e = m % 4;
+            word |= o << (16 * (t % 2) + (t < 2 ? kOff14Real[e] : kOff14Dummy[e]));
+          }
+          memcpy(blob + d->off_offs + rec * pob, &word, 4);
+        }
+      }
+  }
   return SGEMV_OK;
 }
 
@@ -157,7 +224,9 @@ extern "C" int sgemv_layout(const sgemv_desc* d, const uint8_t* vals, const uint
                 const uint32_t code = (vrow[j >> 1] >> (4 * (j & 1))) & 0xFu;
                 word |= code << (4 * kNib24[k]);
               }
-              memcpy(cb + rec * pcb + 4 * dw, &word, 4);
+              // 16-byte slices: dwords 0-3 of all 64 lanes, then dwords 4-7
+              const int64_t rec0 = ((int64_t)b * C + c) * 64;
+              memcpy(cb + rec0 * pcb + ((dw / 4) * 64 + r + 16 * q) * 16 + 4 * (dw % 4), &word, 4);
             }
             continue;
           }

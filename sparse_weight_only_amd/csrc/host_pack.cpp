@@ -7,7 +7,8 @@
 // importance of eq. (3), first term, in sgemv_prune), §3.2 "Adaptive group
 // quantization" (finer groups for sensitive channels; sensitivity from the
 // first term of eq. (3)), §1 "our core idea" (FP16 -> INT4 weight-only) and
-// the first contribution item (index-compressed 2bit-CSR). Build with
+// the first contribution item (index-compressed 2bit-CSR; sgemv_pack_fp16
+// keeps the kept values in FP16, the form before INT4). Build with
 // -ffp-contract=off: every FP64 operation is rounded on its own.
 #include <math.h>
 #include <stdlib.h>
@@ -212,6 +213,32 @@ extern "C" int sgemv_pack(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
     rowptr[n] = (int32_t)((int64_t)n * kpr);
   }
   gptr[N] = (int32_t)gbase;
+  rowptr[N] = (int32_t)((int64_t)N * kpr);
+  return SGEMV_OK;
+}
+
+extern "C" int sgemv_pack_fp16(const uint16_t* w, int32_t N, int32_t K, int32_t nk,
+                               uint16_t* vals16, uint8_t* offs, int32_t* rowptr) {
+  if (!w || !vals16 || !offs || !rowptr || !shape_ok(N, K, nk) || nk == 4) return SGEMV_EINVAL;
+  if (!all_finite(w, (int64_t)N * K)) return SGEMV_EINVAL;
+  const int kpr = K * nk / 4;
+  std::vector<uint8_t> ko(kpr);
+  for (int32_t n = 0; n < N; ++n) {
+    const uint16_t* row = w + (int64_t)n * K;
+    uint16_t* vrow = vals16 + (int64_t)n * kpr;
+    for (int32_t j = 0; j < K / 4; ++j) {
+      int kept[4];
+      select_kept(row + 4 * j, nk, kept);
+      for (int i = 0; i < nk; ++i) {
+        vrow[j * nk + i] = row[4 * j + kept[i]];
+        ko[j * nk + i] = (uint8_t)kept[i];
+      }
+    }
+    uint8_t* orow = offs + (int64_t)n * (kpr / 4);
+    for (int j = 0; j < kpr / 4; ++j)
+      orow[j] = (uint8_t)(ko[4 * j] | (ko[4 * j + 1] << 2) | (ko[4 * j + 2] << 4) | (ko[4 * j + 3] << 6));
+    rowptr[n] = (int32_t)((int64_t)n * kpr);
+  }
   rowptr[N] = (int32_t)((int64_t)N * kpr);
   return SGEMV_OK;
 }

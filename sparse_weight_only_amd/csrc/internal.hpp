@@ -71,6 +71,7 @@ inline int bucket(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
 inline bool valid_nk(int nk) { return nk == 1 || nk == 2 || nk == 4; }
 inline int piece_code_bytes(int nk) { return 8 * nk; }    // 16 (1:4), 32 (2:4) or 64 (dense) nibbles
 inline int piece_offs_bytes(int nk) { return nk == 4 ? 0 : 4 * nk; }   // 2 bits per kept element
+inline int piece_value16_bytes(int nk) { return 32 * nk; }                // FP16-valued form
 
 // Launch geometry for (chunks per row, row blocks, batch): how the column
 // chunks of a row block are split over the waves of its workgroup and how

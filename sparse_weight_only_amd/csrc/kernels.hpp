@@ -26,4 +26,8 @@ inline GroupFn get_group_kernel(int nk, int imax, int xmax) {
        : nk == 4 ? get_group_kernel_nk4(imax, xmax) : nullptr;
 }
 
+// The FP16-valued form (nk 1 or 2).
+KernelFn get_f16_kernel(int nk, int imax, int xmax);
+GroupFn get_f16_group_kernel(int nk, int imax, int xmax);
+
 }  // namespace sgemv_dev

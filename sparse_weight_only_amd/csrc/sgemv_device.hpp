@@ -147,11 +147,15 @@ __device__ __forceinline__ int words_before(const KParams& p, int i) {
   return s;
 }
 
-// Row block rb of the layer p, computed by the whole workgroup.
-template <int NK, int IMAX, int XMAX>
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+
+// Row block rb of the layer p, computed by the whole workgroup. V16: the
+// FP16-valued form (the kept values themselves, no groups, no scale/zero).
+template <int NK, int IMAX, int XMAX, bool V16 = false>
 __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
+  static_assert(!V16 || NK == 1 || NK == 2, "FP16 values exist at 2:4 and 1:4");
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int CB = 8 * NK, OB = 4 * NK;   // bytes of one piece's codes and offsets
+  constexpr int CB = V16 ? 32 * NK : 8 * NK, OB = 4 * NK;   // bytes of one piece's values and offsets
   // the wave index is the same on every lane: keep it (and what follows
   // from it) in scalar registers
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -200,7 +204,9 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
   __builtin_amdgcn_sched_barrier(0);
 
   // weights of every chunk of the wave
-  typedef typename std::conditional<NK == 4, u32x8, typename std::conditional<NK == 2, u32x4, u32x2>::type>::type CodeT;
+  typedef typename std::conditional<
+      V16, typename std::conditional<NK == 2, u32x16, u32x8>::type,
+      typename std::conditional<NK == 4, u32x8, typename std::conditional<NK == 2, u32x4, u32x2>::type>::type>::type CodeT;
   typedef typename std::conditional<NK == 2, u32x2, uint32_t>::type OffT;
   CodeT cv[IMAX];
   OffT ov[IMAX];
@@ -213,10 +219,28 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
     // scale|zero: padding rows of a last, partial block read whatever words
     // follow (or zeros past the blob); their sums are never stored
     const uint32_t so = p.off_sz + (sz_block + (uint32_t)c * rec_words + sz_lane) * 4u;
-    if constexpr (NK == 4) {
+    // records of 64 lanes x CB bytes stored as 16-byte slices: slice k of all
+    // lanes, then slice k + 1 (each load below reads 1 KiB contiguously)
+    const uint32_t slice0 = p.off_codes + (rec - lane) * CB + lane * 16u;
+    if constexpr (V16) {
+      // FP16 values: 64 (2:4) or 32 (1:4) bytes per lane and chunk
+      const u32x4 v0 = bload4<kStream>(rbuf, slice0, off);
+      const u32x4 v1 = bload4<kStream>(rbuf, slice0 + 1024u, off);
+      if constexpr (NK == 2) {
+        const u32x4 v2 = bload4<kStream>(rbuf, slice0 + 2048u, off);
+        const u32x4 v3 = bload4<kStream>(rbuf, slice0 + 3072u, off);
+        const u32x8 lo = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const u32x8 hi = __builtin_shufflevector(v2, v3, 0, 1, 2, 3, 4, 5, 6, 7);
+        cv[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+        ov[i] = bload2<kStream>(rbuf, p.off_offs + rec * OB, off);
+      } else {
+        cv[i] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        ov[i] = bload1<kStream>(rbuf, p.off_offs + rec * OB, off);
+      }
+    } else if constexpr (NK == 4) {
       // dense ablation: 32 bytes of codes, no offsets
-      const u32x4 lo = bload4<kStream>(rbuf, p.off_codes + rec * CB, off);
-      const u32x4 hi = bload4<kStream>(rbuf, p.off_codes + rec * CB + 16u, off);
+      const u32x4 lo = bload4<kStream>(rbuf, slice0, off);
+      const u32x4 hi = bload4<kStream>(rbuf, slice0 + 1024u, off);
       cv[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       ov[i] = 0u;
     } else if constexpr (NK == 2) {
@@ -226,7 +250,8 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
       cv[i] = bload2<kStream>(rbuf, p.off_codes + rec * CB, off);
       ov[i] = bload1<kStream>(rbuf, p.off_offs + rec * OB, off);
     }
-    sv[i] = bload2<kStream>(rbuf, so, off);
+    if constexpr (!V16) sv[i] = bload2<kStream>(rbuf, so, off);
+    else sv[i] = u32x2{0u, 0u};
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -271,6 +296,25 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
       const h8 blo = *reinterpret_cast<const h8*>(xc + 16 * t);
       const h8 bhi = *reinterpret_cast<const h8*>(xc + 16 * t + 128);
       const h16 Bop = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      if constexpr (V16) {
+        // FP16 values: at 2:4 the 8 values of step t are the operand as
+        // stored; at 1:4 the 4 values go to slots 0, 2, 5, 7 (0 elsewhere),
+        // as the dequantised 1:4 operand
+        uint32_t a0, a1, a2, a3, idx;
+        if constexpr (NK == 2) {
+          a0 = cv[i][4 * t]; a1 = cv[i][4 * t + 1]; a2 = cv[i][4 * t + 2]; a3 = cv[i][4 * t + 3];
+          idx = ov[i][t >> 1];
+        } else {
+          const uint32_t e01 = cv[i][2 * t], e23 = cv[i][2 * t + 1];
+          a0 = e01 & 0xFFFFu; a1 = e01 >> 16; a2 = e23 << 16; a3 = e23 & 0xFFFF0000u;
+          idx = t < 2 ? ov[i] : idx2;
+        }
+        const h2 A0 = as_h2(a0), A1 = as_h2(a1), A2 = as_h2(a2), A3 = as_h2(a3);
+        const h8 A = {A0.x, A0.y, A1.x, A1.y, A2.x, A2.y, A3.x, A3.y};
+        if (t & 1) acc = smfmac<1>(A, Bop, acc, idx);
+        else acc = smfmac<0>(A, Bop, acc, idx);
+        continue;
+      }
       if constexpr (NK == 4) {
         // dense ablation: the 4 groups of step t as two 2-of-4 operands with
         // constant index fields, in-group positions (0, 1) and (2, 3)
@@ -352,6 +396,11 @@ __global__ __launch_bounds__(1024) void sgemv_kernel(KParams p) {
   if ((int)blockIdx.x >= p.T) return;
   sgemv_block<NK, IMAX, XMAX>(p, (int)blockIdx.x);
 }
+template <int NK, int IMAX, int XMAX>
+__global__ __launch_bounds__(1024) void sgemv_f16_kernel(KParams p) {
+  if ((int)blockIdx.x >= p.T) return;
+  sgemv_block<NK, IMAX, XMAX, true>(p, (int)blockIdx.x);
+}
 
 // One launch, several independent layers with the same N:M choice, batch and
 // chunks per wave: workgroup b computes row block b - first_block[i] of layer
@@ -365,13 +414,21 @@ struct GParams {
 };
 static_assert(sizeof(GParams) <= 4096, "kernel arguments are limited to 4 KiB");
 
-template <int NK, int IMAX, int XMAX>
-__global__ __launch_bounds__(1024) void sgemv_group_kernel(GParams g) {
+template <int NK, int IMAX, int XMAX, bool V16>
+__device__ __forceinline__ void group_block(const GParams& g) {
   const int b = (int)blockIdx.x;
   if (b >= g.first_block[g.count]) return;
   int i = 0;
   while (i + 1 < g.count && b >= g.first_block[i + 1]) ++i;
-  sgemv_block<NK, IMAX, XMAX>(g.t[i], b - g.first_block[i]);
+  sgemv_block<NK, IMAX, XMAX, V16>(g.t[i], b - g.first_block[i]);
+}
+template <int NK, int IMAX, int XMAX>
+__global__ __launch_bounds__(1024) void sgemv_group_kernel(GParams g) {
+  group_block<NK, IMAX, XMAX, false>(g);
+}
+template <int NK, int IMAX, int XMAX>
+__global__ __launch_bounds__(1024) void sgemv_f16_group_kernel(GParams g) {
+  group_block<NK, IMAX, XMAX, true>(g);
 }
 
 }  // namespace sgemv_dev

@@ -15,11 +15,15 @@ using sgemv_dev::KParams;
 
 namespace {
 
-// The descriptor must be one that sgemv_describe can produce.
+// The descriptor must be one that sgemv_describe (or sgemv_describe_fp16) can produce.
 bool desc_consistent(const sgemv_desc* d) {
+  if (d->value_format == 1) {
+    sgemv_desc chk;
+    return sgemv_describe_fp16(d->N, d->K, d->nk, &chk) == SGEMV_OK && memcmp(&chk, d, sizeof chk) == 0;
+  }
   if (d->N < 1 || d->K < kChunkCols || d->K % kChunkCols || !valid_nk(d->nk)) return false;
   const int32_t C = d->K / kChunkCols, T = (d->N + kBlockRows - 1) / kBlockRows;
-  if (C > kMaxChunks || d->chunks != C || d->n_blocks != T || d->reserved != 0) return false;
+  if (C > kMaxChunks || d->chunks != C || d->n_blocks != T || d->value_format != 0) return false;
   int64_t rows = 0, groups = 0;
   for (int c = 0; c < 4; ++c) {
     if (d->class_rows[c] < 0) return false;
@@ -96,7 +100,7 @@ int make_group_plan(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_pla
     const sgemv_desc* d = tasks[i].desc;
     if (!d) return SGEMV_EINVAL;
     if (!desc_consistent(d)) return SGEMV_ESIZE;
-    if (d->nk != tasks[0].desc->nk) return SGEMV_EINVAL;
+    if (d->nk != tasks[0].desc->nk || d->value_format != tasks[0].desc->value_format) return SGEMV_EINVAL;
     blocks += d->n_blocks;
     cmax = d->chunks > cmax ? d->chunks : cmax;
   }
@@ -133,7 +137,8 @@ extern "C" int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* 
   if (rc) return rc;
   if (!aligned(blob_dev, x_dev, y_dev)) return SGEMV_EALIGN;
   const KParams p = make_params(d, blob_dev, x_dev, y_dev, B, L);
-  KernelFn fn = sgemv_dev::get_kernel(d->nk, L.imax, L.xmax);
+  KernelFn fn = d->value_format == 1 ? sgemv_dev::get_f16_kernel(d->nk, L.imax, L.xmax)
+                                     : sgemv_dev::get_kernel(d->nk, L.imax, L.xmax);
   if (!fn) return SGEMV_ESIZE;
   if (pl.lds_bytes > 65536) {
     if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds_bytes) != hipSuccess)
@@ -164,7 +169,8 @@ extern "C" int sgemv_run_group(const sgemv_task* tasks, int32_t count, int32_t B
     g.t[i] = make_params(t.desc, t.blob_dev, t.x_dev, t.y_dev, B, L);
     g.first_block[i + 1] = g.first_block[i] + t.desc->n_blocks;
   }
-  GroupFn fn = sgemv_dev::get_group_kernel(tasks[0].desc->nk, L.imax, L.xmax);
+  GroupFn fn = tasks[0].desc->value_format == 1 ? sgemv_dev::get_f16_group_kernel(tasks[0].desc->nk, L.imax, L.xmax)
+                                               : sgemv_dev::get_group_kernel(tasks[0].desc->nk, L.imax, L.xmax);
   if (!fn) return SGEMV_ESIZE;
   if (pl.lds_bytes > 65536) {
     if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds_bytes) != hipSuccess)

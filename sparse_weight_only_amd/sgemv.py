@@ -36,7 +36,7 @@ class Desc(ctypes.Structure):
         ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("nk", ctypes.c_int32),
         ("n_blocks", ctypes.c_int32), ("chunks", ctypes.c_int32),
         ("g_min", ctypes.c_int32), ("g_max", ctypes.c_int32),
-        ("class_rows", ctypes.c_int32 * 4), ("reserved", ctypes.c_int32),
+        ("class_rows", ctypes.c_int32 * 4), ("value_format", ctypes.c_int32),
         ("kept", ctypes.c_int64), ("vals_bytes", ctypes.c_int64), ("offs_bytes", ctypes.c_int64),
         ("n_groups", ctypes.c_int64), ("off_codes", ctypes.c_int64), ("off_offs", ctypes.c_int64),
         ("off_perm", ctypes.c_int64), ("off_sz", ctypes.c_int64), ("blob_bytes", ctypes.c_int64),
@@ -84,6 +84,9 @@ def lib():
         L.sgemv_select_groups.argtypes = [P, i32, i32, i32, P, i32, f64, i32, i32, P]
         L.sgemv_pack.argtypes = [P, i32, i32, i32, P, P, P, P, P, P, P]
         L.sgemv_prune.argtypes = [P, i32, i32, i32, P, i32, P]
+        L.sgemv_describe_fp16.argtypes = [i32, i32, i32, ctypes.POINTER(Desc)]
+        L.sgemv_pack_fp16.argtypes = [P, i32, i32, i32, P, P, P]
+        L.sgemv_layout_fp16.argtypes = [ctypes.POINTER(Desc), P, P, P]
         L.sgemv_layout.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P, P]
         L.sgemv_run.argtypes = [ctypes.POINTER(Desc), P, P, P, i32, P]
         L.sgemv_plan.argtypes = [ctypes.POINTER(Desc), i32, ctypes.POINTER(Plan)]
@@ -92,7 +95,8 @@ def lib():
         L.sgemv_strerror.argtypes = [ctypes.c_int]
         L.sgemv_strerror.restype = ctypes.c_char_p
         for f in ("sgemv_describe", "sgemv_select_groups", "sgemv_pack", "sgemv_prune", "sgemv_layout", "sgemv_run", "sgemv_plan",
-                  "sgemv_run_group", "sgemv_plan_group"):
+                  "sgemv_run_group", "sgemv_plan_group", "sgemv_describe_fp16", "sgemv_pack_fp16",
+                  "sgemv_layout_fp16"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -187,6 +191,36 @@ def layout(desc: Desc, canon: dict) -> np.ndarray:
     return blob
 
 
+def describe_fp16(N: int, K: int, nk: int) -> Desc:
+    """Descriptor of the FP16-valued form (no groups)."""
+    d = Desc()
+    _check(lib().sgemv_describe_fp16(N, K, nk, ctypes.byref(d)), "sgemv_describe_fp16")
+    return d
+
+
+def pack_fp16(w16: np.ndarray, nk: int) -> dict:
+    """Dense FP16 [N, K] -> N:M prune -> FP16-valued 2bit-CSR arrays."""
+    w = _host(np.asarray(w16).view(np.uint16), np.uint16)
+    N, K = w.shape
+    if K % 256 or nk not in (1, 2):
+        _check(SGEMV_EINVAL, "sgemv_pack_fp16")
+    kpr = K * nk // 4
+    vals16 = np.empty((N, kpr), dtype=np.uint16)
+    offs = np.empty((N, kpr // 4), dtype=np.uint8)
+    rowptr = np.empty(N + 1, dtype=np.int32)
+    _check(lib().sgemv_pack_fp16(_ptr(w), N, K, nk, _ptr(vals16), _ptr(offs), _ptr(rowptr)), "sgemv_pack_fp16")
+    return {"N": N, "K": K, "nk": nk, "vals16": vals16, "offs": offs, "rowptr": rowptr}
+
+
+def layout_fp16(desc: Desc, canon16: dict) -> np.ndarray:
+    """FP16-valued canonical arrays -> kernel-layout blob (host uint8 array)."""
+    blob = np.empty(desc.blob_bytes, dtype=np.uint8)
+    v = _host(canon16["vals16"], np.uint16)
+    o = _host(canon16["offs"], np.uint8)
+    _check(lib().sgemv_layout_fp16(ctypes.byref(desc), _ptr(v), _ptr(o), _ptr(blob)), "sgemv_layout_fp16")
+    return blob
+
+
 def run(desc: Desc, blob_dev: int, x_dev: int, y_dev: int, B: int, stream: int = 0) -> None:
     """Enqueue y = W' x on ``stream`` (raw device pointers as ints)."""
     _check(lib().sgemv_run(ctypes.byref(desc), ctypes.c_void_p(blob_dev), ctypes.c_void_p(x_dev),
@@ -222,7 +256,8 @@ def plan_group(tasks, B: int) -> Plan:
 
 
 def algorithmic_bytes(desc: Desc, B: int) -> int:
-    """Bytes the method must move per call: codes + offsets + FP16 scale/zero + x + y."""
+    """Bytes the method must move per call: values (INT4 codes or FP16) + offsets
+    + FP16 scale/zero (INT4 form only) + x + y."""
     return int(desc.vals_bytes + desc.offs_bytes + 4 * desc.n_groups + 2 * B * desc.K + 2 * B * desc.N)
 
 
@@ -253,6 +288,15 @@ class SparseGemvLayer:
         canon = pack(w16, nk, group_size)
         desc = describe(N, K, nk, group_size)
         return cls(desc, canon, layout(desc, canon), device)
+
+    @classmethod
+    def from_dense_fp16(cls, w16: np.ndarray, nk: int, device="cuda") -> "SparseGemvLayer":
+        """The FP16-valued form: N:M pruning only, the kept values in FP16."""
+        w16 = np.asarray(w16, dtype=np.float16)
+        N, K = w16.shape
+        canon = pack_fp16(w16, nk)
+        desc = describe_fp16(N, K, nk)
+        return cls(desc, canon, layout_fp16(desc, canon), device)
 
     def run(self, x, y=None, stream=None):
         """y = W' x for a torch FP16 tensor x of shape [K] or [B, K] on the device."""

@@ -304,3 +304,56 @@ def test_dense_ablation_within_tolerance(L):
         err = ogemv.normalized_error(y, y_ref, D)
         say(f"  B={B}: normalised error {err:.3e}")
         assert err <= TOL
+
+
+@pytest.mark.parametrize("nk", [2, 1])
+@pytest.mark.parametrize("N,K", [(300, 4096), (77, 11008), (16, 256), (1000, 2048), (17, 32768)])
+def test_fp16_form_exact_arithmetic(nk, N, K):
+    """FP16-valued form on grid weights (multiples of 2^-6, |w| <= 1/8) and 64
+    entries of x in {-1, 1}: every partial sum and y (|y| <= 8) are exact, so y
+    must equal the oracle's bits."""
+    rng = np.random.default_rng(N + K + 7 * nk)
+    W = (rng.integers(-8, 9, (N, K)) * 2.0 ** -6).astype(np.float16)
+    layer = sg.SparseGemvLayer.from_dense_fp16(W, nk)
+    say(f"case fp16 form exact nk={nk} N={N} K={K}")
+    for B in (1, 3, 16):
+        X = np.zeros((B, K), np.float16)
+        for b in range(B):
+            idx = rng.choice(K, size=min(64, K), replace=False)
+            X[b, idx] = rng.choice([-1.0, 1.0], len(idx))
+        y = run_checked(layer, X)
+        y_ref, D, _ = oracle_y(layer.canon, X)
+        want = y_ref.astype(np.float16)
+        assert np.array_equal(want.astype(np.float64), y_ref), "reference not exact"
+        assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), B
+
+
+@pytest.mark.parametrize("L", synth.cfg3(), ids=lambda L: L.name + "_fp16")
+def test_fp16_form_mlp_within_tolerance(L):
+    from oracle import pack as opack
+    W = L.W()
+    say(f"case fp16 form {L.name}")
+    layer = sg.SparseGemvLayer.from_dense_fp16(W, L.nk)
+    co = opack.pack_fp16_canonical(W, L.nk)
+    assert np.array_equal(layer.canon["vals16"], co["vals16"])
+    for B in (1, 4):
+        X = L.X(B)
+        y = run_checked(layer, X)
+        y_ref, D, _ = oracle_y(layer.canon, X)
+        err = ogemv.normalized_error(y, y_ref, D)
+        say(f"  B={B}: normalised error {err:.3e}")
+        assert err <= TOL
+
+
+def test_fp16_form_group_launch():
+    rng = np.random.default_rng(5)
+    layers, Xs = [], []
+    for N, K in [(600, 4096), (33, 4096), (256, 1024)]:
+        W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+        layers.append(sg.SparseGemvLayer.from_dense_fp16(W, 2))
+        Xs.append(rng.standard_normal((2, K)).astype(np.float16))
+    say("case fp16 form group launch")
+    ys = _run_group_checked(layers, Xs, 2)
+    for layer, X, y in zip(layers, Xs, ys):
+        y_ref, D, _ = oracle_y(layer.canon, X)
+        assert ogemv.normalized_error(y, y_ref, D) <= TOL

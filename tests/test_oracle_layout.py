@@ -167,6 +167,40 @@ def test_hand_placed_bytes_dense():
     # 2,6,10,14,3,7,11,15
     assert u32_at(blob, 4) == 0xFB73EA62
     # lane 16 (columns 64..127): dword 7 = columns 112..127, positions 2, 3:
-    # elements 114,115,118,119,122,123,126,127 -> codes 2,3,6,7,10,11,14,15
-    assert u32_at(blob, 16 * 32 + 28) == 0xFB73EA62
+    # elements 114,115,118,119,122,123,126,127 -> codes 2,3,6,7,10,11,14,15;
+    # dwords 4-7 of every lane follow dwords 0-3 of every lane (1 KiB slices)
+    assert u32_at(blob, 1024 + 16 * 16 + 12) == 0xFB73EA62
     assert u32_at(blob, 2304) == 0x48003C00
+
+
+@pytest.mark.parametrize("N,K,nk", [(7, 256, 2), (19, 768, 2), (33, 512, 1), (5, 2816, 1)])
+def test_fp16_form_decode_inverts_build(N, K, nk):
+    rng = np.random.default_rng(N + nk)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    c = pack.pack_fp16_canonical(W, nk)
+    L = layout.build16(c)
+    q16, o = layout.decode16(L["blob"], N, K, nk)
+    _, o_ref = pack.unpack_bytes(np.zeros((N, 1), np.uint8), c["offs"])
+    assert np.array_equal(q16, c["vals16"]) and np.array_equal(o, o_ref)
+    off = L["offsets"]
+    assert off["blob_bytes"] == layout._align(off["perm"] + 64 * (-(-N // 16)))
+
+
+def test_fp16_form_hand_placed_values():
+    # one row, 2:4: lane 16 (columns 64..127) holds kept elements 32..63 in
+    # order: 64 bytes; its first value is element 32
+    N, K, nk = 1, 256, 2
+    W = np.zeros((N, K), np.float16)
+    W[0, 0::4] = np.arange(64, dtype=np.float16)          # column 4j holds j, kept with column 4j+1 (0)
+    c = pack.pack_fp16_canonical(W, nk)
+    L = layout.build16(c)
+    blob = L["blob"]
+    # element 32 = column 64 (value 16), element 33 = column 65 (value 0);
+    # slice 0 (values 0-7) of lane 16 sits at 16 * 16
+    v = np.frombuffer(blob[16 * 16: 16 * 16 + 8].tobytes(), "<u2").view(np.float16)
+    assert v.tolist() == [16.0, 0.0, 17.0, 0.0]
+    # slice 1 of lane 16 (elements 40..47 = columns 80, 81, ...) follows all 64 lanes' slice 0
+    v = np.frombuffer(blob[1024 + 16 * 16: 1024 + 16 * 16 + 4].tobytes(), "<u2").view(np.float16)
+    assert v.tolist() == [20.0, 0.0]
+    # 64 lanes x 64 bytes of values, then 64 lanes x 8 bytes of offsets
+    assert L["offsets"]["offs"] == 4096 and L["offsets"]["perm"] == 4096 + 512

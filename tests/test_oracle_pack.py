@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from oracle import pack, prune, quant, groups
+from oracle import pack, prune, quant, groups, gemv
 from conftest import read_golden
 
 
@@ -75,3 +75,23 @@ def test_rejects_bad_groups():
     for gs in ([48, 128], [128], [512, 128]):
         with pytest.raises(ValueError):
             pack.pack_canonical(W, 2, gs)
+
+
+def test_fp16_valued_form_hand_example_and_round_trip():
+    """FP16-valued 2bit-CSR: kept values as FP16 bits, same offsets as the INT4 form."""
+    W = np.zeros((1, 256), dtype=np.float16)
+    W[0, :8] = [0.5, -2.0, 0.25, 1.0, 0.0, -0.0, 3.0, -3.0]
+    c = pack.pack_fp16_canonical(W, 2)
+    # group 0 keeps -2 (col 1) and 1 (col 3); group 1 keeps 3 and -3 (cols 6, 7):
+    # values -2, 1, 3, -3 (bits 0xC000, 0x3C00, 0x4200, 0xC200), offsets 1, 3, 2, 3
+    assert c["vals16"][0, :4].tolist() == [0xC000, 0x3C00, 0x4200, 0xC200]
+    assert c["offs"][0, 0] == (1 | 3 << 2 | 2 << 4 | 3 << 6)
+    c1 = pack.pack_fp16_canonical(W, 1)
+    assert c1["vals16"][0, :2].tolist() == [0xC000, 0x4200]          # -2 at col 1, 3 at col 6 (tie -> lower)
+    rng = np.random.default_rng(4)
+    Wr = (rng.standard_normal((9, 512)) * 0.02).astype(np.float16)
+    for nk in (1, 2):
+        c = pack.pack_fp16_canonical(Wr, nk)
+        assert c["vals16"].size * 2 == 9 * 512 * nk // 4 * 2 and c["offs"].size == 9 * 512 * nk // 16
+        _, mask = prune.nm_prune(Wr, nk)
+        assert np.array_equal(gemv.dequant_dense(c), np.where(mask, Wr.astype(np.float64), 0.0))

@@ -202,7 +202,7 @@ def test_plan_rejects_bad_batch_and_descriptor():
         with pytest.raises(sg.SgemvError) as e:
             sg.plan(d, B)
         assert e.value.code == sg.sgemv.SGEMV_EINVAL
-    for field, delta in [("n_blocks", 1), ("chunks", -1), ("n_groups", 1), ("off_perm", 256), ("reserved", 1),
+    for field, delta in [("n_blocks", 1), ("chunks", -1), ("n_groups", 1), ("off_perm", 256), ("value_format", 1),
                          ("blob_bytes", 256)]:
         bad = sg.Desc.from_buffer_copy(d)
         setattr(bad, field, getattr(bad, field) + delta)
@@ -352,3 +352,55 @@ def test_dense_ablation_mlp_shapes(L):
     MLP shapes: groups, canonical arrays and blob bit-exact against the oracle."""
     import dataclasses
     check_layer(dataclasses.replace(L, nk=4, name=L.name.replace("2of4", "dense")))
+
+
+@pytest.mark.parametrize("N,K,nk", [(4096, 4096, 2), (11008, 4096, 1), (77, 1280, 1), (33, 11008, 2), (1, 256, 2)])
+def test_fp16_form_matches_oracle(N, K, nk):
+    """FP16-valued form: canonical arrays, descriptor and blob bit-exact against the oracle."""
+    rng = np.random.default_rng(N + K + nk)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    c = sg.pack_fp16(W, nk)
+    co = opack.pack_fp16_canonical(W, nk)
+    for k in ("vals16", "offs", "rowptr"):
+        assert np.array_equal(c[k], co[k]), k
+    d = sg.describe_fp16(N, K, nk)
+    lay = olayout.build16(co)
+    off = lay["offsets"]
+    assert (d.value_format, d.n_groups, list(d.class_rows), d.g_min, d.g_max) == (1, 0, [0, 0, 0, 0], 0, 0)
+    assert (d.kept, d.vals_bytes, d.offs_bytes) == (N * K * nk // 4, N * K * nk // 2, N * K * nk // 16)
+    assert (d.off_codes, d.off_offs, d.off_perm, d.blob_bytes) == (off["values"], off["offs"], off["perm"], off["blob_bytes"])
+    assert np.array_equal(sg.layout_fp16(d, c), lay["blob"])
+    pl = sg.plan(d, 1)
+    assert pl.grid == -(-N // 16)
+
+
+def test_fp16_form_errors():
+    E = sg.sgemv
+    W = np.zeros((8, 256), np.float16)
+    with pytest.raises(sg.SgemvError) as e:
+        sg.describe_fp16(8, 256, 4)
+    assert e.value.code == E.SGEMV_EINVAL
+    with pytest.raises(sg.SgemvError):
+        sg.pack_fp16(W, 4)
+    W[2, 3] = np.inf
+    with pytest.raises(sg.SgemvError):
+        sg.pack_fp16(W, 2)
+    W[2, 3] = 0
+    d16 = sg.describe_fp16(8, 256, 2)
+    d4 = sg.describe(8, 256, 2, np.full(8, 128, np.int32))
+    c16 = sg.pack_fp16(W, 2)
+    with pytest.raises(sg.SgemvError) as e:                    # an INT4 descriptor
+        sg.layout_fp16(d4, c16)
+    assert e.value.code == E.SGEMV_EINVAL
+    with pytest.raises(sg.SgemvError):                         # an FP16 descriptor in the INT4 layout
+        sg.layout(d16, sg.pack(W, 2, np.full(8, 128, np.int32)))
+    bad = sg.Desc.from_buffer_copy(d16)
+    bad.n_groups = 1
+    with pytest.raises(sg.SgemvError) as e:
+        sg.plan(bad, 1)
+    assert e.value.code == E.SGEMV_ESIZE
+    # one launch cannot mix the two value formats
+    fake = [(d16, 0x1000, 0x1000, 0x1000), (d4, 0x2000, 0x1000, 0x2000)]
+    with pytest.raises(sg.SgemvError) as e:
+        sg.plan_group(fake, 1)
+    assert e.value.code == E.SGEMV_EINVAL
