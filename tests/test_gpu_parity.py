@@ -357,3 +357,31 @@ def test_fp16_form_group_launch():
     for layer, X, y in zip(layers, Xs, ys):
         y_ref, D, _ = oracle_y(layer.canon, X)
         assert ogemv.normalized_error(y, y_ref, D) <= TOL
+
+
+@pytest.mark.parametrize("nk", [2, 1])
+def test_large_layer_sampled_rows(nk):
+    """A large layer (262144 x 4096: blobs of 0.25-0.45 GB, offsets far into
+    the 32-bit range) in the launch geometry the workloads use; the oracle
+    checks 64 sampled rows (uniform groups keep rows independent, so the
+    oracle packs only those rows)."""
+    from oracle import pack as opack
+    N, K = 262144, 4096
+    rng = np.random.default_rng(99 + nk)
+    # 8192 random rows, tiled: the address arithmetic sees every row block
+    W = np.tile((rng.standard_normal((8192, K), dtype=np.float32) * 0.02).astype(np.float16), (N // 8192, 1))
+    gs = np.full(N, 128, np.int32)
+    say(f"case large layer nk={nk} N={N} K={K}")
+    layer = make_layer(W, nk, gs)
+    say(f"  blob {layer.desc.blob_bytes / 2**20:.0f} MiB, grid {sg.plan(layer.desc, 1).grid}")
+    X = rng.standard_normal((2, K)).astype(np.float16)
+    y = run_checked(layer, X)
+    rows = np.concatenate([[0, 1, N - 1, N - 16, N // 2], rng.choice(N, 59, replace=False)])
+    co = opack.pack_canonical(W[rows], nk, gs[rows])
+    Wd = ogemv.dequant_dense(co)
+    y_ref, D = ogemv.gemv(Wd, X), ogemv.abs_dot(Wd, X)
+    err = ogemv.normalized_error(y[:, rows], y_ref, D)
+    say(f"  sampled normalised error {err:.3e}")
+    assert err <= TOL
+    del layer
+    torch.cuda.empty_cache()
