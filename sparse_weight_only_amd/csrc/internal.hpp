@@ -100,7 +100,9 @@ inline Launch launch_geometry(int C, int T, int B) {
   L.phase = ph;
   L.xloads = (B * ph * 32 + 63) / 64;
   L.xmax = bucket(L.xloads);
-  L.lds = (int64_t)L.waves * B * ph * 512 + (int64_t)B * kBlockRows * kMaxWaves * 4;
+  // per wave: B rows of x, each ph * 512 bytes plus 16 bytes of padding
+  // (the one-vector kernel of the INT4 form leaves the padding unused)
+  L.lds = (int64_t)L.waves * B * (ph * 512 + 16) + (int64_t)B * kBlockRows * kMaxWaves * 4;
   return L;
 }
 

@@ -26,6 +26,18 @@ inline GroupFn get_group_kernel(int nk, int imax, int xmax) {
        : nk == 4 ? get_group_kernel_nk4(imax, xmax) : nullptr;
 }
 
+// Kernels for exactly one vector (INT4 form, nk 1 or 2; xmax 1, 2 or 4).
+KernelFn get_b1_kernel_nk1(int imax, int xmax);
+KernelFn get_b1_kernel_nk2(int imax, int xmax);
+GroupFn get_b1_group_kernel_nk1(int imax, int xmax);
+GroupFn get_b1_group_kernel_nk2(int imax, int xmax);
+inline KernelFn get_b1_kernel(int nk, int imax, int xmax) {
+  return nk == 2 ? get_b1_kernel_nk2(imax, xmax) : nk == 1 ? get_b1_kernel_nk1(imax, xmax) : nullptr;
+}
+inline GroupFn get_b1_group_kernel(int nk, int imax, int xmax) {
+  return nk == 2 ? get_b1_group_kernel_nk2(imax, xmax) : nk == 1 ? get_b1_group_kernel_nk1(imax, xmax) : nullptr;
+}
+
 // The FP16-valued form (nk 1 or 2).
 KernelFn get_f16_kernel(int nk, int imax, int xmax);
 GroupFn get_f16_group_kernel(int nk, int imax, int xmax);

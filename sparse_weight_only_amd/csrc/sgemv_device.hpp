@@ -151,7 +151,7 @@ typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
 // Row block rb of the layer p, computed by the whole workgroup. V16: the
 // FP16-valued form (the kept values themselves, no groups, no scale/zero).
-template <int NK, int IMAX, int XMAX, bool V16 = false>
+template <int NK, int IMAX, int XMAX, bool V16 = false, bool ONE = false>
 __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
   static_assert(!V16 || NK == 1 || NK == 2, "FP16 values exist at 2:4 and 1:4");
   extern __shared__ __align__(16) unsigned char smem[];
@@ -255,17 +255,31 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  _Float16* xs = reinterpret_cast<_Float16*>(smem) + w * (B * span16 * 8);
-  float* part = reinterpret_cast<float*>(smem + W * B * span16 * 16);
-  // small batches: the slots of waves this workgroup does not have hold +0,
-  // so that the final sum reads all 16 slots without a test per slot (the
-  // sum is then on the critical path of few lanes, and short)
-  if (B <= 4)
+  // x slice of the wave: B rows of span16 16-byte units; with several
+  // vectors each row is padded by one unit, so that the 16 batch columns of
+  // a B-operand read fall in different LDS banks (ONE: the kernel for one
+  // vector, whose lanes all read row 0, a broadcast)
+  constexpr int xpad = ONE ? 0 : 1;
+  const int xrow_units = span16 + xpad;
+  _Float16* xs = reinterpret_cast<_Float16*>(smem) + w * (B * xrow_units * 8);
+  // partial sums of the waves, 16 slots per (b, row): for one vector
+  // part[b][row][wave] (the final sum reads 4 x 16 bytes per entry), for
+  // several part[wave][b][row] (a lane stores its 4 rows with one
+  // conflict-free 16-byte write; the 16 lanes of a batch would otherwise hit
+  // one bank). Slots of waves this workgroup does not have hold +0, so that
+  // the final sum reads all 16 slots without a test per slot.
+  constexpr bool slot_major = ONE;
+  float* part = reinterpret_cast<float*>(smem + W * B * xrow_units * 16);
+  if constexpr (slot_major) {
     for (int e = tid; e < 16 * B * 16; e += blockDim.x)   // (batch row, row, slot)
       if ((e & 15) >= W) part[e] = 0.f;
+  } else {
+    for (int e = tid; e < (16 - W) * B * 4; e += blockDim.x)
+      reinterpret_cast<f4*>(part)[W * B * 4 + e] = f4{0.f, 0.f, 0.f, 0.f};
+  }
   const uint32_t magic = opaque_vgpr(0x64006400u);
   const int bcol = (lane & 15) < B ? (lane & 15) : 0;
-  const _Float16* xrow = xs + __umul24((uint32_t)bcol, (uint32_t)(span16 * 8)) + 64 * (q >> 1) + 8 * (q & 1);
+  const _Float16* xrow = xs + __umul24((uint32_t)bcol, (uint32_t)(xrow_units * 8)) + 64 * (q >> 1) + 8 * (q & 1);
   f4 acc = {0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
@@ -277,7 +291,7 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
 #pragma unroll
       for (int j = 0; j < XMAX; ++j) {
         const int u = lane + 64 * j;
-        if (u < B * span16) reinterpret_cast<u32x4*>(xs)[u] = xv[j];
+        if (u < B * span16) reinterpret_cast<u32x4*>(xs)[u + ((u >> span_log) & -xpad)] = xv[j];   // row b at b * xrow_units
       }
       __builtin_amdgcn_wave_barrier();
       if (i + PH < ncw) issue_x(i + PH);
@@ -357,33 +371,39 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
     }
   }
 
-  // 4. partial sums of the waves: part[b][row][wave]; lane (b = lane % 16,
-  // q) holds rows 4q .. 4q + 3 of column b
+  // 4. partial sums of the waves: lane (b = lane % 16, q) holds rows
+  // 4q .. 4q + 3 of column b
   if ((lane & 15) < B) {
-    float* pp = part + ((lane & 15) * 16 + 4 * q) * 16 + w;
-    pp[0] = acc.x;
-    pp[16] = acc.y;
-    pp[32] = acc.z;
-    pp[48] = acc.w;
+    if constexpr (slot_major) {
+      float* pp = part + ((lane & 15) * 16 + 4 * q) * 16 + w;
+      pp[0] = acc.x;
+      pp[16] = acc.y;
+      pp[32] = acc.z;
+      pp[48] = acc.w;
+    } else {
+      reinterpret_cast<f4*>(part)[(w * B + (lane & 15)) * 4 + q] = acc;
+    }
   }
   __syncthreads();
   // entries e = 16 b + row; the block size is a multiple of 16, so every
-  // entry of this lane has row tid % 16
+  // entry of this lane has row tid % 16; the waves are added in order
   for (int e = tid; e < 16 * B; e += blockDim.x) {
-    const int b = e >> 4, rr = e & 15;
-    const f4* pv = reinterpret_cast<const f4*>(part + (b * 16 + rr) * 16);
-    const f4 v0 = pv[0], v1 = pv[1], v2 = pv[2], v3 = pv[3];
-    const float vv[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
-                          v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
-    float s = 0.f;
-    if (B <= 4) {
+    float vv[16];
+    if constexpr (slot_major) {
+      const f4* pv = reinterpret_cast<const f4*>(part + e * 16);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s += vv[v];   // slots W.. hold +0
+      for (int k = 0; k < 4; ++k) {
+        const f4 v4 = pv[k];
+        vv[4 * k] = v4.x; vv[4 * k + 1] = v4.y; vv[4 * k + 2] = v4.z; vv[4 * k + 3] = v4.w;
+      }
     } else {
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (v < W) s += vv[v];
+      for (int v = 0; v < 16; ++v) vv[v] = part[v * B * 16 + e];   // (wave v, b, row) = v * 16B + e
     }
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s += vv[v];   // slots of absent waves hold +0
+    const int b = e >> 4;
     const int n = (int)orow;
     // B * N < 2^31 (the blob size bounds N), so 32-bit indexing is enough
     if (n >= 0 && n < p.N) p.y[(uint32_t)(b * p.N + n)] = __builtin_bit_cast(uint16_t, (_Float16)s);
@@ -395,6 +415,12 @@ template <int NK, int IMAX, int XMAX>
 __global__ __launch_bounds__(1024) void sgemv_kernel(KParams p) {
   if ((int)blockIdx.x >= p.T) return;
   sgemv_block<NK, IMAX, XMAX>(p, (int)blockIdx.x);
+}
+// The same for exactly one vector (B = 1).
+template <int NK, int IMAX, int XMAX>
+__global__ __launch_bounds__(1024) void sgemv_b1_kernel(KParams p) {
+  if ((int)blockIdx.x >= p.T) return;
+  sgemv_block<NK, IMAX, XMAX, false, true>(p, (int)blockIdx.x);
 }
 template <int NK, int IMAX, int XMAX>
 __global__ __launch_bounds__(1024) void sgemv_f16_kernel(KParams p) {
@@ -414,13 +440,17 @@ struct GParams {
 };
 static_assert(sizeof(GParams) <= 4096, "kernel arguments are limited to 4 KiB");
 
-template <int NK, int IMAX, int XMAX, bool V16>
+template <int NK, int IMAX, int XMAX, bool V16, bool ONE = false>
 __device__ __forceinline__ void group_block(const GParams& g) {
   const int b = (int)blockIdx.x;
   if (b >= g.first_block[g.count]) return;
   int i = 0;
   while (i + 1 < g.count && b >= g.first_block[i + 1]) ++i;
-  sgemv_block<NK, IMAX, XMAX, V16>(g.t[i], b - g.first_block[i]);
+  sgemv_block<NK, IMAX, XMAX, V16, ONE>(g.t[i], b - g.first_block[i]);
+}
+template <int NK, int IMAX, int XMAX>
+__global__ __launch_bounds__(1024) void sgemv_b1_group_kernel(GParams g) {
+  group_block<NK, IMAX, XMAX, false, true>(g);
 }
 template <int NK, int IMAX, int XMAX>
 __global__ __launch_bounds__(1024) void sgemv_group_kernel(GParams g) {

@@ -138,7 +138,8 @@ extern "C" int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* 
   if (!aligned(blob_dev, x_dev, y_dev)) return SGEMV_EALIGN;
   const KParams p = make_params(d, blob_dev, x_dev, y_dev, B, L);
   KernelFn fn = d->value_format == 1 ? sgemv_dev::get_f16_kernel(d->nk, L.imax, L.xmax)
-                                     : sgemv_dev::get_kernel(d->nk, L.imax, L.xmax);
+              : (B == 1 && d->nk != 4)  ? sgemv_dev::get_b1_kernel(d->nk, L.imax, L.xmax)
+                                        : sgemv_dev::get_kernel(d->nk, L.imax, L.xmax);
   if (!fn) return SGEMV_ESIZE;
   if (pl.lds_bytes > 65536) {
     if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds_bytes) != hipSuccess)
@@ -169,8 +170,10 @@ extern "C" int sgemv_run_group(const sgemv_task* tasks, int32_t count, int32_t B
     g.t[i] = make_params(t.desc, t.blob_dev, t.x_dev, t.y_dev, B, L);
     g.first_block[i + 1] = g.first_block[i] + t.desc->n_blocks;
   }
-  GroupFn fn = tasks[0].desc->value_format == 1 ? sgemv_dev::get_f16_group_kernel(tasks[0].desc->nk, L.imax, L.xmax)
-                                               : sgemv_dev::get_group_kernel(tasks[0].desc->nk, L.imax, L.xmax);
+  const int nk0 = tasks[0].desc->nk;
+  GroupFn fn = tasks[0].desc->value_format == 1 ? sgemv_dev::get_f16_group_kernel(nk0, L.imax, L.xmax)
+              : (B == 1 && nk0 != 4)             ? sgemv_dev::get_b1_group_kernel(nk0, L.imax, L.xmax)
+                                                 : sgemv_dev::get_group_kernel(nk0, L.imax, L.xmax);
   if (!fn) return SGEMV_ESIZE;
   if (pl.lds_bytes > 65536) {
     if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds_bytes) != hipSuccess)

@@ -118,7 +118,7 @@ def _bench_layer_kernels() -> dict:
         d = sg.describe(L.N, L.K, L.nk, gs)
         pl = sg.plan(d, 1)
         bucket = lambda n: 1 if n <= 1 else 2 if n <= 2 else 4 if n <= 4 else 8
-        name = f"sgemv_kernel<{L.nk}, {bucket(pl.chunks_per_wave)}, {bucket(pl.x_loads)}>"
+        name = f"sgemv_b1_kernel<{L.nk}, {bucket(pl.chunks_per_wave)}, {bucket(pl.x_loads)}>"
         res[L.name] = (name, int(pl.grid * pl.block))
     return res
 

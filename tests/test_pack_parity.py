@@ -190,7 +190,7 @@ def test_launch_plan_covers_every_chunk_once(seed):
             assert 1 <= pl.phase_chunks <= pl.chunks_per_wave
             assert pl.phase_chunks & (pl.phase_chunks - 1) == 0          # a power of two
             assert pl.x_loads == -(-(B * pl.phase_chunks * 32) // 64) and pl.x_loads <= 8
-            assert pl.lds_bytes == pl.waves * B * pl.phase_chunks * 512 + B * 16 * 16 * 4
+            assert pl.lds_bytes == pl.waves * B * (pl.phase_chunks * 512 + 16) + B * 16 * 16 * 4
             assert pl.lds_bytes <= 160 * 1024
             assert pl.reserved == 0
 
@@ -255,7 +255,7 @@ def test_group_plan_and_host_errors():
                 assert pl.grid == sum(d.n_blocks for d in ds)
                 assert pl.block == 64 * pl.waves and 1 <= pl.waves <= 16
                 assert (pl.waves - 1) * pl.chunks_per_wave < cmax <= pl.waves * pl.chunks_per_wave
-                assert pl.lds_bytes == pl.waves * B * pl.phase_chunks * 512 + B * 16 * 16 * 4
+                assert pl.lds_bytes == pl.waves * B * (pl.phase_chunks * 512 + 16) + B * 16 * 16 * 4
             # a group of one is planned like the single call
             for d in descs[nk]:
                 a, b = sg.plan_group(fake([d]), B), sg.plan(d, B)
