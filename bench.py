@@ -46,7 +46,6 @@ Prints one JSON line. ``--gpus N`` with N > 1 is refused: this build runs on
 one GPU.
 """
 import argparse
-import hashlib
 import json
 import os
 import statistics
@@ -80,11 +79,8 @@ def log(*a):
 
 
 def kernel_source_hash():
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "sparse_weight_only_amd", "csrc"))):
-        with open(os.path.join(ROOT, "sparse_weight_only_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    from sparse_weight_only_amd.profiling import kernel_source_hash as h
+    return h()
 
 
 def read_traffic(kernel_hash, layer_name):

@@ -35,6 +35,14 @@
 //     positions.
 // Large batches stage x in phases of `phase` chunks, prefetching the next
 // phase's slice while the current one is computed.
+//
+// Variants of the same block body (template parameters):
+//  - NK = 4: the dense INT4 ablation, each 16-column step as two 2-of-4
+//    operands with constant index fields (positions (0,1) and (2,3));
+//  - V16: the FP16-valued form, the stored values are the A operand (2:4) or
+//    fill its slots 0, 2, 5, 7 (1:4); no scale/zero;
+//  - ONE: exactly one vector (no x padding, slot-major partial sums);
+//  - the group kernels run the body for the row blocks of up to 32 layers.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

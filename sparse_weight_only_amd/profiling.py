@@ -16,6 +16,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 from collections import defaultdict
@@ -24,12 +25,20 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 REF_KIB = 64 * 1024          # the reference copy: 64 MiB each way
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and blank space, so that the hash follows the code."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the library sources (code only: comment edits keep recorded counters valid)."""
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
