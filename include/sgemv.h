@@ -201,7 +201,7 @@ int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* x_dev,
 
 /* What sgemv_run enqueues for a layer and a batch (filled by sgemv_plan). */
 typedef struct sgemv_plan_t {
-  int64_t grid;            /* workgroups launched: one per row block                  */
+  int64_t grid;            /* workgroups launched: ceil(row blocks / row_blocks)      */
   int64_t lds_bytes;       /* dynamic LDS per workgroup (x slices and wave partials)  */
   int32_t block;           /* lanes per workgroup: 64 * waves                         */
   int32_t waves;           /* waves per workgroup; wave w owns column chunks           */
@@ -209,7 +209,8 @@ typedef struct sgemv_plan_t {
   int32_t chunks_per_wave;
   int32_t phase_chunks;    /* chunks whose x slice is staged in LDS at once           */
   int32_t x_loads;         /* 16-byte x loads per lane and phase                      */
-  int32_t reserved;        /* zero                                                    */
+  int32_t row_blocks;      /* row blocks per workgroup: 1, or 2 / 4 for 4+ vectors on */
+                           /* an INT4 layer with many row blocks (x read once for all) */
 } sgemv_plan_t;
 
 /* sgemv_plan - describe the launch sgemv_run would make for (d, B) without

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libsgemv.so")
 HOST_SRCS = ["host_pack.cpp", "host_layout.cpp"]
-HIP_SRCS = ["sgemv_k_nk1.hip", "sgemv_k_nk2.hip", "sgemv_k_nk4.hip", "sgemv_k_f16.hip", "sgemv_launch.hip"]
+HIP_SRCS = ["sgemv_k_nk1.hip", "sgemv_k_nk2.hip", "sgemv_k_nk4.hip", "sgemv_k_f16.hip", "sgemv_k_rb.hip", "sgemv_launch.hip"]
 
 
 def _hipcc() -> str:

@@ -76,9 +76,10 @@ inline int piece_value16_bytes(int nk) { return 32 * nk; }                // FP1
 // Launch geometry for (chunks per row, row blocks, batch): how the column
 // chunks of a row block are split over the waves of its workgroup and how
 // many chunks of x are staged in LDS at once.
-struct Launch { int waves, cpw, imax, phase, xloads, xmax; int64_t lds; };
+struct Launch { int waves, cpw, imax, phase, xloads, xmax, rb; int64_t lds; };
 inline Launch launch_geometry(int C, int T, int B) {
   Launch L;
+  L.rb = 1;
   // up to 4 vectors, two chunks per wave where that keeps the workgroup
   // within 16 waves: a wave with fewer loads to issue starts computing
   // sooner, which hides more of the dequantisation under the data phase.
@@ -103,6 +104,41 @@ inline Launch launch_geometry(int C, int T, int B) {
   // per wave: B rows of x, each ph * 512 bytes plus 16 bytes of padding
   // (the one-vector kernel of the INT4 form leaves the padding unused)
   L.lds = (int64_t)L.waves * B * (ph * 512 + 16) + (int64_t)B * kBlockRows * kMaxWaves * 4;
+  return L;
+}
+
+// Several vectors on a layer with many row blocks: rb row blocks per
+// workgroup, so that each wave loads its x slices once for all rb blocks (the
+// x traffic from L2 falls rb-fold; at 16 vectors the x of a 4096-column layer
+// is 128 KiB per workgroup, five times the weights of one row block). The
+// weights of rb x 2 pieces are held in registers, and the partial sums keep
+// one slot per wave. Measured on the 11008 x 4096 layers (688 row blocks):
+// 4 blocks per workgroup take 15 % off a call at 16 vectors and 7 % at 8, and
+// add 10 % at 4 (2 blocks: no better at 8, worse at 16). So: rb = 4 from 8
+// vectors on, where K <= 4096 (at most 8 waves of two chunks) and the merged
+// grid still has 160 or more workgroups; rb = 1 otherwise.
+inline int pick_row_blocks(int C, int T, int B) {
+  return B >= 8 && C <= 16 && (int64_t)T >= 4 * 160 ? 4 : 1;
+}
+constexpr int kMaxWavesRb = 8;             // waves per workgroup with several row blocks (256 VGPRs a lane)
+inline Launch launch_geometry_rb(int C, int T, int B, int rb) {
+  Launch L = launch_geometry(C, T, B);
+  if (rb <= 1) return L;
+  // at most 8 waves, at least two chunks per wave
+  int cpw = (C + kMaxWavesRb - 1) / kMaxWavesRb;
+  if (cpw < 2) cpw = 2;
+  L.rb = rb;
+  L.cpw = cpw;
+  L.waves = (C + cpw - 1) / cpw;
+  L.imax = bucket(cpw);
+  int ph = 1;
+  while (ph * 2 <= cpw && B * ph * 2 <= 16) ph *= 2;
+  L.phase = ph;
+  L.xloads = (B * ph * 32 + 63) / 64;
+  L.xmax = bucket(L.xloads);
+  // x slices as above; partial sums: one slot per wave for every (vector,
+  // block, row); the blocks' original row indices
+  L.lds = (int64_t)L.waves * B * (ph * 512 + 16) + (int64_t)L.waves * rb * B * kBlockRows * 4 + (int64_t)rb * kBlockRows * 4;
   return L;
 }
 

@@ -38,6 +38,10 @@ inline GroupFn get_b1_group_kernel(int nk, int imax, int xmax) {
   return nk == 2 ? get_b1_group_kernel_nk2(imax, xmax) : nk == 1 ? get_b1_group_kernel_nk1(imax, xmax) : nullptr;
 }
 
+// Several vectors, rb row blocks per workgroup (INT4 form, nk 1 or 2; rb 4,
+// imax 2, xmax 8).
+KernelFn get_rb_kernel(int nk, int imax, int xmax, int rb);
+
 // The FP16-valued form (nk 1 or 2).
 KernelFn get_f16_kernel(int nk, int imax, int xmax);
 GroupFn get_f16_group_kernel(int nk, int imax, int xmax);

@@ -43,6 +43,8 @@
 //    fill its slots 0, 2, 5, 7 (1:4); no scale/zero;
 //  - ONE: exactly one vector (no x padding, slot-major partial sums);
 //  - the group kernels run the body for the row blocks of up to 32 layers.
+// A second body (sgemv_block_rb) computes RB row blocks per workgroup for
+// batches of several vectors, loading each x slice once for all of them.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -418,6 +420,184 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
   }
 }
 
+// Row blocks rb0 .. rb0 + RB - 1 of the layer p (INT4 form, 2:4 or 1:4,
+// several vectors), computed by the whole workgroup. The steps are those of
+// sgemv_block; what differs: each wave holds the weights of RB x IMAX pieces
+// in registers and uses every x operand it reads from LDS for the RB blocks,
+// so the x slice of a chunk is loaded from L2 once per RB blocks; the
+// partial sums keep one slot per wave (part[wave][b][block][row]) and are
+// added in a loop over the waves; the blocks' original row indices go
+// through LDS. Blocks at or beyond T (the last workgroup) read zeros and
+// store nothing.
+template <int NK, int IMAX, int XMAX, int RB>
+__device__ __forceinline__ void sgemv_block_rb(const KParams& p, const int rb0) {
+  static_assert(NK == 1 || NK == 2, "sparse INT4 forms");
+  static_assert(RB == 2 || RB == 4, "row blocks per workgroup");
+  constexpr int RBLOG = RB == 4 ? 2 : 1;
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int CB = 8 * NK, OB = 4 * NK;   // bytes of one piece's codes and offsets
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int W = blockDim.x >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int B = p.B, PH = p.phase;
+  const auto rbuf = make_rsrc(p.blob, p.blob_bytes);
+  const auto rx = make_rsrc(p.x, (uint32_t)(B * p.K * 2));
+  const int c0 = w * p.cpw;
+  const int ncw = p.C - c0 < p.cpw ? (p.C - c0 > 0 ? p.C - c0 : 0) : p.cpw;   // chunks of this wave
+
+  // 0. original index of row tid of the RB blocks (lanes tid < 16 RB)
+  const uint32_t orow = tid < 16 * RB && rb0 * 16 + tid < 16 * p.T
+                            ? bload1<kCached>(rbuf, p.off_perm + (uint32_t)(rb0 * 16 + tid) * 4u)
+                            : 0xFFFFFFFFu;
+
+  // 1. x slice of the first phase (as in sgemv_block)
+  const int span16 = PH * 32;
+  const int span_log = 5 + (31 - __builtin_clz((unsigned)PH));
+  u32x4 xv[XMAX];
+  auto issue_x = [&](int first) {
+    const int lim = (ncw - first < PH ? ncw - first : PH) * 32;
+#pragma unroll
+    for (int j = 0; j < XMAX; ++j) {
+      const int u = lane + 64 * j, b = u >> span_log, cu = u & (span16 - 1);
+      const bool ok = b < B && cu < lim;
+      xv[j] = bload4<kCached>(rx, ok ? (__umul24((uint32_t)b, (uint32_t)p.K) + (uint32_t)((c0 + first) * 256 + cu * 8)) * 2u
+                                     : kOutOfRange);
+    }
+  };
+  issue_x(0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // per block: this lane's group size class and scale|zero words (as in
+  // sgemv_block); then the weights of every (block, chunk) of the wave
+  typedef typename std::conditional<NK == 2, u32x4, u32x2>::type CodeT;
+  typedef typename std::conditional<NK == 2, u32x2, uint32_t>::type OffT;
+  bool g32[RB];
+  CodeT cv[RB][IMAX];
+  OffT ov[RB][IMAX];
+  u32x2 sv[RB][IMAX];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) {
+    const int rb = rb0 + j;
+    const uint32_t blk_off = rb < p.T ? 0u : kOutOfRange;   // wave-uniform
+    const int row = rb * 16 + r;
+    const int cls = (row >= p.cls_row[1]) + (row >= p.cls_row[2]) + (row >= p.cls_row[3]);
+    const int wb0 = words_before(p, rb * 16);
+    const uint32_t rec_words = (uint32_t)(words_before(p, rb * 16 + 16) - wb0);
+    const int cls_first = (rb * 16 >= p.cls_row[1]) + (rb * 16 >= p.cls_row[2]) + (rb * 16 >= p.cls_row[3]);
+    const bool one_class = rec_words == (uint32_t)(16 * (8 >> cls_first));
+    const uint32_t sz_row = one_class ? (uint32_t)(r * (8 >> cls_first)) : (uint32_t)(words_before(p, row) - wb0);
+    const uint32_t sz_lane = sz_row + (uint32_t)((64 * q) >> (5 + cls));
+    const uint32_t sz_block = (uint32_t)wb0 * (uint32_t)p.C;
+    g32[j] = cls == 0;
+#pragma unroll
+    for (int i = 0; i < IMAX; ++i) {
+      const int c = c0 + i;
+      const uint32_t off = i < ncw ? blk_off : kOutOfRange;
+      const uint32_t rec = (uint32_t)(rb * p.C + c) * 64u + lane;
+      const uint32_t so = p.off_sz + (sz_block + (uint32_t)c * rec_words + sz_lane) * 4u;
+      if constexpr (NK == 2) {
+        cv[j][i] = bload4<kStream>(rbuf, p.off_codes + rec * CB, off);
+        ov[j][i] = bload2<kStream>(rbuf, p.off_offs + rec * OB, off);
+      } else {
+        cv[j][i] = bload2<kStream>(rbuf, p.off_codes + rec * CB, off);
+        ov[j][i] = bload1<kStream>(rbuf, p.off_offs + rec * OB, off);
+      }
+      sv[j][i] = bload2<kStream>(rbuf, so, off);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // x slice of the wave in LDS, rows padded by one 16-byte unit (as in
+  // sgemv_block); partial sums part[wave][b][block][row]; original rows
+  const int xrow_units = span16 + 1;
+  _Float16* xs = reinterpret_cast<_Float16*>(smem) + w * (B * xrow_units * 8);
+  float* part = reinterpret_cast<float*>(smem + W * B * xrow_units * 16);
+  int* perm_s = reinterpret_cast<int*>(part + W * RB * B * 16);
+  const uint32_t magic = opaque_vgpr(0x64006400u);
+  const int bcol = (lane & 15) < B ? (lane & 15) : 0;
+  const _Float16* xrow = xs + __umul24((uint32_t)bcol, (uint32_t)(xrow_units * 8)) + 64 * (q >> 1) + 8 * (q & 1);
+  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  f4 acc[RB];
+#pragma unroll
+  for (int j = 0; j < RB; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int i = 0; i < IMAX; ++i) {
+    if (i >= ncw) break;
+    const int slot = i % PH;
+    if (slot == 0) {
+      // 2. stage this phase's x slice, prefetch the next
+#pragma unroll
+      for (int j = 0; j < XMAX; ++j) {
+        const int u = lane + 64 * j;
+        if (u < B * span16) reinterpret_cast<u32x4*>(xs)[u + (u >> span_log)] = xv[j];   // row b at b * xrow_units
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (i + PH < ncw) issue_x(i + PH);
+    }
+    const _Float16* xc = xrow + 256 * slot;
+    Deq d0[RB], d1[RB];
+    uint32_t idx2[RB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      d0[j] = deq_consts(sv[j][i].x);
+      d1[j] = deq_consts(g32[j] ? sv[j][i].y : sv[j][i].x);
+      idx2[j] = 0u;
+      if constexpr (NK == 1) idx2[j] = ((ov[j][i] & 0x33333333u) << 2) | ((ov[j][i] >> 2) & 0x33333333u);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // 3. the x operand of step t, once for the RB blocks
+      const h8 blo = *reinterpret_cast<const h8*>(xc + 16 * t);
+      const h8 bhi = *reinterpret_cast<const h8*>(xc + 16 * t + 128);
+      const h16 Bop = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+#pragma unroll
+      for (int j = 0; j < RB; ++j) {
+        const Deq& d = t < 2 ? d0[j] : d1[j];
+        uint32_t a0, a1, a2, a3, idx;
+        if constexpr (NK == 2) {
+          const uint32_t cw = cv[j][i][t], c8 = cw >> 8;
+          a0 = deq_lo(cw, magic, d);
+          a1 = deq_hi(cw, magic, d);
+          a2 = deq_lo(c8, magic, d);
+          a3 = deq_hi(c8, magic, d);
+          idx = ov[j][i][t >> 1];
+        } else {
+          const uint32_t cw = (t & 1) ? (cv[j][i][t >> 1] >> 8) : cv[j][i][t >> 1];
+          const h2 q02 = as_h2((cw & 0x000F000Fu) | magic) + d.c1;
+          const h2 q13 = __builtin_elementwise_fma(as_h2((cw & 0x00F000F0u) | magic), sixteenth, d.c16);
+          a0 = as_u32(q02 * d.s_lo);
+          a2 = as_u32(q02 * d.s_hi);
+          a1 = as_u32(q13 * d.s_lo);
+          a3 = as_u32(q13 * d.s_hi);
+          idx = t < 2 ? ov[j][i] : idx2[j];
+        }
+        const h2 A0 = as_h2(a0), A1 = as_h2(a1), A2 = as_h2(a2), A3 = as_h2(a3);
+        const h8 A = {A0.x, A0.y, A1.x, A1.y, A2.x, A2.y, A3.x, A3.y};
+        if (t & 1) acc[j] = smfmac<1>(A, Bop, acc[j], idx);
+        else acc[j] = smfmac<0>(A, Bop, acc[j], idx);
+      }
+    }
+  }
+
+  // 4. partial sums: lane (b, q) stores rows 4q .. 4q + 3 of each block
+  if ((lane & 15) < B) {
+#pragma unroll
+    for (int j = 0; j < RB; ++j) reinterpret_cast<f4*>(part)[((w * B + (lane & 15)) * RB + j) * 4 + q] = acc[j];
+  }
+  if (tid < 16 * RB) perm_s[tid] = (int)orow;
+  __syncthreads();
+  // entries e = (b * RB + j) * 16 + row, the waves added in order
+  for (int e = tid; e < 16 * B * RB; e += blockDim.x) {
+    float s = 0.f;
+    for (int v = 0; v < W; ++v) s += part[v * B * RB * 16 + e];
+    const int b = (e >> 4) >> RBLOG, j = (e >> 4) & (RB - 1);
+    const int n = perm_s[j * 16 + (e & 15)];
+    // B * N < 2^31 (the blob size bounds N), so 32-bit indexing is enough
+    if (n >= 0 && n < p.N) p.y[(uint32_t)(b * p.N + n)] = __builtin_bit_cast(uint16_t, (_Float16)s);
+  }
+}
+
 // One launch, one layer: workgroup b computes row block b.
 template <int NK, int IMAX, int XMAX>
 __global__ __launch_bounds__(1024) void sgemv_kernel(KParams p) {
@@ -429,6 +609,14 @@ template <int NK, int IMAX, int XMAX>
 __global__ __launch_bounds__(1024) void sgemv_b1_kernel(KParams p) {
   if ((int)blockIdx.x >= p.T) return;
   sgemv_block<NK, IMAX, XMAX, false, true>(p, (int)blockIdx.x);
+}
+// Several vectors, RB row blocks per workgroup: workgroup b computes row
+// blocks RB*b .. RB*b + RB - 1. At most 8 waves, so that the weights of
+// RB x IMAX pieces stay in registers.
+template <int NK, int IMAX, int XMAX, int RB>
+__global__ __launch_bounds__(512) void sgemv_rb_kernel(KParams p) {
+  if ((int)blockIdx.x * RB >= p.T) return;
+  sgemv_block_rb<NK, IMAX, XMAX, RB>(p, (int)blockIdx.x * RB);
 }
 template <int NK, int IMAX, int XMAX>
 __global__ __launch_bounds__(1024) void sgemv_f16_kernel(KParams p) {

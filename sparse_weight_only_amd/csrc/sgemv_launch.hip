@@ -48,12 +48,16 @@ int make_plan(const sgemv_desc* d, int32_t B, sgemv_plan_t* pl, Launch* geo) {
   if (!d || !pl) return SGEMV_EINVAL;
   if (B < 1 || B > 16) return SGEMV_EINVAL;
   if (!desc_consistent(d)) return SGEMV_ESIZE;
-  const Launch L = launch_geometry(d->chunks, d->n_blocks, B);
+  // several row blocks per workgroup: INT4 sparse forms only
+  const int rb = d->value_format == 0 && d->nk != 4 ? pick_row_blocks(d->chunks, d->n_blocks, B) : 1;
+  const Launch L = launch_geometry_rb(d->chunks, d->n_blocks, B, rb);
   if (L.waves < 1 || L.waves > kMaxWaves || L.cpw > kMaxChunksPerWave || L.xloads > 8) return SGEMV_ESIZE;
   if (L.lds > 160 * 1024 || (L.phase & (L.phase - 1)) != 0) return SGEMV_ESIZE;
+  if (L.rb > 1 && (L.rb * L.imax > kMaxChunksPerWave || L.waves > kMaxWavesRb)) return SGEMV_ESIZE;
   sgemv_plan_t q;
   memset(&q, 0, sizeof q);
-  q.grid = d->n_blocks;
+  q.grid = (d->n_blocks + L.rb - 1) / L.rb;
+  q.row_blocks = L.rb;
   q.lds_bytes = L.lds;
   q.block = 64 * L.waves;
   q.waves = L.waves;
@@ -111,6 +115,7 @@ int make_group_plan(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_pla
   sgemv_plan_t q;
   memset(&q, 0, sizeof q);
   q.grid = blocks;
+  q.row_blocks = 1;
   q.lds_bytes = L.lds;
   q.block = 64 * L.waves;
   q.waves = L.waves;
@@ -138,6 +143,7 @@ extern "C" int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* 
   if (!aligned(blob_dev, x_dev, y_dev)) return SGEMV_EALIGN;
   const KParams p = make_params(d, blob_dev, x_dev, y_dev, B, L);
   KernelFn fn = d->value_format == 1 ? sgemv_dev::get_f16_kernel(d->nk, L.imax, L.xmax)
+              : L.rb > 1                ? sgemv_dev::get_rb_kernel(d->nk, L.imax, L.xmax, L.rb)
               : (B == 1 && d->nk != 4)  ? sgemv_dev::get_b1_kernel(d->nk, L.imax, L.xmax)
                                         : sgemv_dev::get_kernel(d->nk, L.imax, L.xmax);
   if (!fn) return SGEMV_ESIZE;

@@ -179,6 +179,53 @@ def test_every_launch_geometry(nk, N, K):
         assert err <= TOL, (B, err)
 
 
+@pytest.mark.parametrize("nk", [2, 1])
+@pytest.mark.parametrize("N,K", [(16390, 4096), (10250, 2048), (10255, 768)])
+def test_several_row_blocks_per_workgroup(nk, N, K):
+    """Batches of 8+ vectors on layers with many row blocks take the kernel
+    that computes 4 row blocks per workgroup (x loaded once for all of them).
+    These shapes give a last workgroup with fewer blocks than it computes, a
+    last block of fewer than 16 rows, a last wave with one chunk and blocks of
+    different group sizes in one workgroup: bit for bit where the arithmetic
+    is exact, within tolerance on Gaussian inputs, and the same bits on a
+    second run. At 4 vectors the same layer takes one block per workgroup."""
+    rng = np.random.default_rng(N + K + nk)
+    T = -(-N // 16)
+    gs = rng.choice([32, 64, 128, 256], N).astype(np.int32)
+    W = np.zeros((N, K), np.float16)
+    for g in np.unique(gs):
+        rows = gs == g
+        W[rows] = grid_weights(int(rows.sum()), K, nk, int(g), rng)
+    layer = make_layer(W, nk, gs)
+    Wd = ogemv.dequant_dense(layer.canon)
+    for B in (4, 8, 9, 16):
+        pl = sg.plan(layer.desc, B)
+        want_rb = 4 if B >= 8 else 1
+        say(f"case row blocks N={N} K={K} nk={nk} B={B} row_blocks={pl.row_blocks} waves={pl.waves} "
+            f"cpw={pl.chunks_per_wave} xloads={pl.x_loads}")
+        assert pl.row_blocks == want_rb and pl.grid == -(-T // want_rb)
+        X = np.zeros((B, K), np.float16)
+        for b in range(B):
+            idx = rng.choice(K, size=64, replace=False)
+            X[b, idx] = rng.choice([-1.0, 1.0], 64)
+        y = run_checked(layer, X)
+        y_ref = ogemv.gemv(Wd, X)
+        want = y_ref.astype(np.float16)
+        assert np.array_equal(want.astype(np.float64), y_ref), "reference not exact"
+        assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), f"B={B}"
+    # Gaussian weights and inputs: tolerance, then determinism
+    Wg = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    layer = make_layer(Wg, nk, gs)
+    Wd = ogemv.dequant_dense(layer.canon)
+    X = rng.standard_normal((16, K)).astype(np.float16)
+    y = run_checked(layer, X)
+    err = ogemv.normalized_error(y, ogemv.gemv(Wd, X), ogemv.abs_dot(Wd, X))
+    say(f"  gaussian B=16: normalised error {err:.3e}")
+    assert err <= TOL
+    y2 = run_checked(layer, X)
+    assert np.array_equal(y.view(np.uint16), y2.view(np.uint16)), "not deterministic"
+
+
 def _run_group_checked(layers, Xs, B, guard=64):
     """One sgemv_run_group launch over layers (each with its own x and guarded y)."""
     import torch

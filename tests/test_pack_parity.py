@@ -170,29 +170,42 @@ def test_error_paths():
 
 @pytest.mark.parametrize("seed", range(4))
 def test_launch_plan_covers_every_chunk_once(seed):
-    """sgemv_plan (host arithmetic only): one workgroup per row block; its waves
-    split the column chunks in whole slices; x phases fit the 8 loads per lane
-    and the LDS holds every wave's slice plus the partial sums."""
+    """sgemv_plan (host arithmetic only): one workgroup per row_blocks row
+    blocks (1, or 4 for 8+ vectors on INT4 sparse layers with K <= 4096 and
+    640+ row blocks); its waves split the column chunks in whole slices; x
+    phases fit the 8 loads per lane, the weights of row_blocks x
+    chunks_per_wave pieces fit the register budget, and the LDS holds every
+    wave's slice plus the partial sums."""
     rng = np.random.default_rng(seed)
-    for _ in range(40):
+    seen = set()
+    for it in range(48):
         nk = int(rng.choice([1, 2, 4]))
         K = 256 * int(rng.choice([1, 2, 3, 4, 5, 11, 16, 43, 64, 65, 128]))
-        N = int(rng.integers(1, 12000))
+        N = int(rng.integers(1, 12000)) if it % 4 else int(rng.integers(8000, 40000))
         gs = rng.choice([32, 64, 128, 256], N).astype(np.int32)
         d = sg.describe(N, K, nk, gs)
         C = K // 256
         for B in (1, 2, 3, 4, 7, 8, 9, 16):
             pl = sg.plan(d, B)
-            assert pl.grid == d.n_blocks == -(-N // 16)
+            rb = pl.row_blocks
+            seen.add(rb)
+            assert rb == (4 if nk != 4 and B >= 8 and C <= 16 and d.n_blocks >= 640 else 1)
+            assert d.n_blocks == -(-N // 16) and pl.grid == -(-d.n_blocks // rb)
             assert pl.block == 64 * pl.waves and 1 <= pl.waves <= 16
             assert 1 <= pl.chunks_per_wave <= 8
+            imax = 1 << (pl.chunks_per_wave - 1).bit_length()
+            assert rb * imax <= 8
             assert (pl.waves - 1) * pl.chunks_per_wave < C <= pl.waves * pl.chunks_per_wave
             assert 1 <= pl.phase_chunks <= pl.chunks_per_wave
             assert pl.phase_chunks & (pl.phase_chunks - 1) == 0          # a power of two
             assert pl.x_loads == -(-(B * pl.phase_chunks * 32) // 64) and pl.x_loads <= 8
-            assert pl.lds_bytes == pl.waves * B * (pl.phase_chunks * 512 + 16) + B * 16 * 16 * 4
+            xs = pl.waves * B * (pl.phase_chunks * 512 + 16)
+            if rb == 1:
+                assert pl.lds_bytes == xs + B * 16 * 16 * 4
+            else:
+                assert pl.lds_bytes == xs + pl.waves * rb * B * 16 * 4 + rb * 16 * 4
             assert pl.lds_bytes <= 160 * 1024
-            assert pl.reserved == 0
+    assert seen == {1, 4}
 
 
 def test_plan_rejects_bad_batch_and_descriptor():
@@ -257,9 +270,14 @@ def test_group_plan_and_host_errors():
                 assert (pl.waves - 1) * pl.chunks_per_wave < cmax <= pl.waves * pl.chunks_per_wave
                 assert pl.lds_bytes == pl.waves * B * (pl.phase_chunks * 512 + 16) + B * 16 * 16 * 4
             # a group of one is planned like the single call
+            # (the single call may merge row blocks; the group launch does not)
             for d in descs[nk]:
                 a, b = sg.plan_group(fake([d]), B), sg.plan(d, B)
-                assert a.as_dict() == b.as_dict()
+                assert a.row_blocks == 1
+                if b.row_blocks == 1:
+                    assert a.as_dict() == b.as_dict()
+                else:
+                    assert a.grid == d.n_blocks and b.grid == -(-d.n_blocks // b.row_blocks)
     # up to 32 layers; 0, 33 and mixed N:M choices are rejected
     small = sg.describe(16, 256, 2, np.full(16, 128, np.int32))
     assert sg.plan_group(fake([small] * 32), 1).grid == 32
