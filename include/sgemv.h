@@ -209,8 +209,9 @@ typedef struct sgemv_plan_t {
   int32_t chunks_per_wave;
   int32_t phase_chunks;    /* chunks whose x slice is staged in LDS at once           */
   int32_t x_loads;         /* 16-byte x loads per lane and phase                      */
-  int32_t row_blocks;      /* row blocks per workgroup: 1, or 2 / 4 for 4+ vectors on */
-                           /* an INT4 layer with many row blocks (x read once for all) */
+  int32_t row_blocks;      /* row blocks per workgroup: 1, or 4 for 8+ vectors on an  */
+                           /* INT4 sparse layer with K <= 4096 and 640+ row blocks    */
+                           /* (each x slice then read once for the 4 blocks)          */
 } sgemv_plan_t;
 
 /* sgemv_plan - describe the launch sgemv_run would make for (d, B) without
