@@ -164,11 +164,14 @@ typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 template <int NK, int IMAX, int XMAX, bool V16 = false, bool ONE = false>
 __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
   static_assert(!V16 || NK == 1 || NK == 2, "FP16 values exist at 2:4 and 1:4");
-  // one vector: waves issue their loads at raised priority, so that a wave
-  // still issuing is not held back by the dequantisation of waves whose
-  // data has arrived (measured: 0.15 us off the four MLP layers at batch 1;
-  // mixed at several vectors, so those keep the normal priority)
+  // waves issue their loads at raised priority, so that a wave still issuing
+  // is not held back by the dequantisation of waves whose data has arrived.
+  // Measured: 0.15 us off the four MLP layers at one vector, 0.3-0.5 us off
+  // the 11008 -> 4096 layers at 16 vectors; at 2-8 vectors it was neutral
+  // or slower, so there the priority stays normal.
+  const bool raise = ONE || (!V16 && p.B >= 16);
   if constexpr (ONE) __builtin_amdgcn_s_setprio(2);
+  else if (raise) __builtin_amdgcn_s_setprio(2);
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int CB = V16 ? 32 * NK : 8 * NK, OB = 4 * NK;   // bytes of one piece's values and offsets
   // the wave index is the same on every lane: keep it (and what follows
@@ -270,6 +273,7 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
   }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (ONE) __builtin_amdgcn_s_setprio(0);
+  else if (raise) __builtin_amdgcn_s_setprio(0);
 
   // x slice of the wave: B rows of span16 16-byte units; with several
   // vectors each row is padded by one unit, so that the 16 batch columns of
