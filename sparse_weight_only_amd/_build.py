@@ -59,7 +59,29 @@ def build(verbose: bool = False, arch: str = "gfx950") -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", "-fPIC", "-o", tmp] + [o for o, _ in jobs], verbose)
     os.replace(tmp, LIB)
+    build_c_driver(verbose)
     return LIB
+
+
+# The tests' plain-C driver of the library (tests/c_abi/sgemv_c_driver.c):
+# built here, beside the library, so that no test compiles anything. Strict
+# C99 against include/sgemv.h; the HIP runtime's C API for device memory.
+REPO = os.path.dirname(HERE)
+C_DRIVER_SRC = os.path.join(REPO, "tests", "c_abi", "sgemv_c_driver.c")
+C_DRIVER = os.path.join(REPO, "tests", "c_abi", "_build", "sgemv_c_driver")
+
+
+def build_c_driver(verbose: bool = False) -> str:
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(_hipcc())))
+    os.makedirs(os.path.dirname(C_DRIVER), exist_ok=True)
+    rel_lib = os.path.relpath(OUT_DIR, os.path.dirname(C_DRIVER))
+    tmp = C_DRIVER + ".tmp"
+    _run(["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic", "-D__HIP_PLATFORM_AMD__",
+          "-I", os.path.join(REPO, "include"), "-isystem", os.path.join(rocm, "include"), C_DRIVER_SRC,
+          "-L", OUT_DIR, "-lsgemv", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+          "-Wl,-rpath,$ORIGIN/" + rel_lib, "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", tmp], verbose)
+    os.replace(tmp, C_DRIVER)
+    return C_DRIVER
 
 
 if __name__ == "__main__":
