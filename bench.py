@@ -27,6 +27,9 @@ Beside the step, the same line reports
   2:4 and 1:4, and as a plain FP16 GEMV through torch (hipBLASLt, launched
   eagerly: a library call stays out of graph capture), at B = 1, cold, with
   the sparse layers' speedups;
+* ``small_configs``: µs and GB/s per call of the single 1024 -> 1024 layer
+  and the 4096 -> 4096 attention projection (2:4, uniform g = 128, B = 1),
+  timed like the per-layer figures;
 * ``beam``: µs and GB/s per call of the beam-batch shapes (up and down of
   decoder layers 0 (2:4) and 4 (1:4)) at B = 4, 8, 16, timed like the
   per-layer figures;
@@ -71,6 +74,7 @@ def parse():
     ap.add_argument("--no-beam", action="store_true", help="skip the beam-batch figures")
     ap.add_argument("--no-decoder", action="store_true", help="skip the 224-GEMV decoder sequence")
     ap.add_argument("--no-ablation", action="store_true", help="skip the dense INT4 / FP16 ablation")
+    ap.add_argument("--no-small", action="store_true", help="skip the 1024x1024 and 4096x4096 layers")
     return ap.parse_args()
 
 
@@ -286,6 +290,30 @@ def main():
             torch.cuda.empty_cache()
         log("beam batches timed")
 
+    # ---- the two single-layer configurations at B = 1: 1024 -> 1024 and the
+    # 4096 -> 4096 attention projection (x with 1 % outlier channels), both
+    # 2:4 with uniform g = 128, timed cold like the MLP layers
+    small = None
+    if not args.no_small:
+        small = {}
+        for L in synth.cfg1() + synth.cfg2():
+            W = L.W()
+            gs = np.full(L.N, synth.G_COARSE, dtype=np.int32)
+            desc = sg.describe(L.N, L.K, L.nk, gs)
+            host = torch.from_numpy(sg.layout(desc, sg.pack(W, L.nk, gs)))
+            R = max(2, -(-COLD_BYTES // desc.blob_bytes))
+            copies = [host.to(dev) for _ in range(R)]
+            x = torch.from_numpy(L.X(1)).to(dev)
+            y = torch.empty((1, L.N), dtype=torch.float16, device=dev)
+            us = per_call_us(desc, copies, x, y, 1, args.layer_calls)
+            nb = sg.algorithmic_bytes(desc, 1)
+            small[L.name] = {"us_per_call": round(us, 3), "bytes": nb, "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                             "pct_hbm_peak": round(100 * nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+                             "cold_copies": R}
+            del copies
+            torch.cuda.empty_cache()
+        log("single-layer configurations timed")
+
     # ---- ablation at B = 1: the same MLP weights as a dense INT4 layer (every
     # element kept, same quantiser and groups policy) and as a plain FP16
     # GEMV through torch (hipBLASLt), each timed cold like the sparse layers
@@ -426,6 +454,8 @@ def main():
     }
     if beam is not None:
         out["beam"] = beam
+    if small is not None:
+        out["small_configs"] = small
     if decoder is not None:
         out["decoder"] = decoder
     if ablation is not None:
