@@ -6,9 +6,10 @@
  * layers, 1:4 for the others), quantised to INT4 with asymmetric group-wise
  * scales whose group size is chosen per output channel, and stored in an
  * index-compressed "2bit-CSR" format; x is FP16 (one vector or a small beam
- * batch) and accumulation is FP32. Source: the page "Efficient LLM ad
- * generation via model compression and parallel verification" (Chinese
- * translation of arXiv 2605.11582), cited as P1 below: §1 ("our core idea"
+ * batch) and accumulation is FP32. Source: the page "Efficient large-model
+ * ad applications through model compression and parallel verification"
+ * (English gloss of its Chinese title; a Chinese translation of arXiv
+ * 2605.11582), cited as P1 below: §1 ("our core idea"
  * and the contribution list), §3.2 "Model compression" (adaptive group
  * quantization, sparsification, eqs. (1)-(3)) and §3.3 "Revised kernel".
  *

@@ -2,8 +2,9 @@
 
 Plain, slow, obviously-correct NumPy (FP64 where floating point is involved)
 implementation of what the SparseGemv path computes, written from the page
-"Efficient LLM ad generation via model compression and parallel verification"
-(Chinese translation of arXiv 2605.11582; cited below as P1) and from the
+"Efficient large-model ad applications through model compression and parallel verification"
+(an English gloss of its Chinese title; the page is a Chinese translation of
+arXiv 2605.11582; cited below as P1) and from the
 plainest readings where that page is silent.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of

@@ -23,9 +23,9 @@
 //  - perm: original row of each sorted row, -1 for padding rows;
 //  - scale|zero<<16 words: records (b, c) in order, each the rows of block b
 //    in order, each with its 256/g words of chunk c (groups c*256/g ..).
-// Reference: the first contribution item of the page "Efficient LLM ad
-// generation via model compression and parallel verification" (translation
-// of arXiv 2605.11582), which introduces the index-compressed 2bit-CSR format
+// Reference: the first contribution item of the page "Efficient large-model
+// ad applications through model compression and parallel verification"
+// (English gloss of its Chinese title; a translation of arXiv 2605.11582), which introduces the index-compressed 2bit-CSR format
 // but leaves its bit layout open.
 #include <algorithm>
 #include <cmath>

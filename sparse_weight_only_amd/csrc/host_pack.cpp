@@ -1,8 +1,9 @@
 // Host packer: N:M pruning, adaptive group choice, asymmetric INT4 group
 // quantisation and the canonical 2bit-CSR arrays.
 //
-// Follows the page "Efficient LLM ad generation via model compression and
-// parallel verification" (translation of arXiv 2605.11582): §3.2
+// Follows the page "Efficient large-model ad applications through model
+// compression and parallel verification" (English gloss of its Chinese title;
+// a translation of arXiv 2605.11582): §3.2
 // "Sparsification" (layer-wise N:M, 2:4 or 1:4; the activation-aware
 // importance of eq. (3), first term, in sgemv_prune), §3.2 "Adaptive group
 // quantization" (finer groups for sensitive channels; sensitivity from the

@@ -2,9 +2,10 @@
 //
 // y = W' x for an N:M-sparse (2:4 or 1:4 along K) INT4 weight matrix with
 // per-group FP16 scale and zero, FP16 activations and FP32 accumulation: the
-// custom weight-only GEMV with mixed sparsity of the page "Efficient LLM ad
-// generation via model compression and parallel verification" (translation
-// of arXiv 2605.11582), §1 (second contribution item) and §3.3 "Revised
+// custom weight-only GEMV with mixed sparsity of the page "Efficient
+// large-model ad applications through model compression and parallel
+// verification" (English gloss of its Chinese title; a translation of arXiv
+// 2605.11582), §1 (second contribution item) and §3.3 "Revised
 // kernel". That section stops before describing its kernel; the design here
 // is our own for CDNA4.
 //
