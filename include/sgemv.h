@@ -205,14 +205,17 @@ typedef struct sgemv_plan_t {
   int64_t grid;            /* workgroups launched: ceil(row blocks / row_blocks)      */
   int64_t lds_bytes;       /* dynamic LDS per workgroup (x slices and wave partials)  */
   int32_t block;           /* lanes per workgroup: 64 * waves                         */
-  int32_t waves;           /* waves per workgroup; wave w owns column chunks           */
-                           /* [w * chunks_per_wave, (w + 1) * chunks_per_wave)        */
+  int32_t waves;           /* waves per workgroup; wave w owns a contiguous range of   */
+                           /* column chunks: chunks_per_wave of them if              */
+                           /* w < full_waves, one less after (fewer at the row end), */
+                           /* starting at w * chunks_per_wave - max(0, w - full_waves) */
   int32_t chunks_per_wave;
   int32_t phase_chunks;    /* chunks whose x slice is staged in LDS at once           */
   int32_t x_loads;         /* 16-byte x loads per lane and phase                      */
   int32_t row_blocks;      /* row blocks per workgroup: 1, or 4 for 8+ vectors on an  */
                            /* INT4 sparse layer with K <= 4096 and 640+ row blocks    */
                            /* (each x slice then read once for the 4 blocks)          */
+  int32_t full_waves;      /* waves that take chunks_per_wave chunks (see waves)      */
 } sgemv_plan_t;
 
 /* sgemv_plan - describe the launch sgemv_run would make for (d, B) without

@@ -76,7 +76,24 @@ inline int piece_value16_bytes(int nk) { return 32 * nk; }                // FP1
 // Launch geometry for (chunks per row, row blocks, batch): how the column
 // chunks of a row block are split over the waves of its workgroup and how
 // many chunks of x are staged in LDS at once.
-struct Launch { int waves, cpw, imax, phase, xloads, xmax, rb; int64_t lds; };
+struct Launch { int waves, cpw, crem, imax, phase, xloads, xmax, rb; int64_t lds; };
+
+// Wave w takes chunks [w * cpw - max(0, w - crem), ...), cpw of them if
+// w < crem, else cpw - 1 (fewer at the end of the row): the waves' ranges
+// are contiguous. The most chunks any of the 4 SIMDs of a workgroup gets,
+// waves being placed on SIMD w % 4.
+inline int simd_max_chunks(int C, int W, int cpw, int crem) {
+  int per[4] = {0, 0, 0, 0};
+  for (int w = 0; w < W; ++w) {
+    const int c0 = w * cpw - (w > crem ? w - crem : 0);
+    const int cmax = cpw - (w >= crem ? 1 : 0);
+    const int n = C - c0 < cmax ? (C - c0 > 0 ? C - c0 : 0) : cmax;
+    per[w & 3] += n;
+  }
+  int m = per[0];
+  for (int k = 1; k < 4; ++k) m = per[k] > m ? per[k] : m;
+  return m;
+}
 inline Launch launch_geometry(int C, int T, int B) {
   Launch L;
   L.rb = 1;
@@ -91,6 +108,21 @@ inline Launch launch_geometry(int C, int T, int B) {
   if ((C + cpw - 1) / cpw > kMaxWaves) cpw = (C + kMaxWaves - 1) / kMaxWaves;
   L.cpw = cpw;
   L.waves = (C + cpw - 1) / cpw;
+  L.crem = L.waves;   // every wave takes cpw chunks, the last one what is left
+  // The dequantisation of a workgroup is bounded by its busiest SIMD. One
+  // more wave, with the chunks split evenly (C % W waves take cpw, the
+  // others cpw - 1), when that lowers the most chunks on a SIMD at the same
+  // cpw: 43 chunks (K = 11008) as 11 waves of 4 put 12 chunks on a SIMD,
+  // 12 waves (7 of 4, 5 of 3) put 11. Measured on the 11008 -> 4096 layers:
+  // 0.11-0.13 us off a call at one vector, 0.1-0.45 us off at 4 and 16
+  // vectors, 0.15 us more at 8 vectors at 1:4.
+  if (L.waves < kMaxWaves) {
+    const int W = L.waves + 1, rem = C % W, c2 = C / W + (rem ? 1 : 0);
+    if (c2 == cpw && simd_max_chunks(C, W, cpw, rem ? rem : W) < simd_max_chunks(C, L.waves, cpw, L.crem)) {
+      L.waves = W;
+      L.crem = rem ? rem : W;
+    }
+  }
   L.imax = bucket(cpw);
   // x of phase chunks staged at once: B * phase <= 16 keeps the staging at
   // most 8 16-byte loads per lane
@@ -130,6 +162,7 @@ inline Launch launch_geometry_rb(int C, int T, int B, int rb) {
   L.rb = rb;
   L.cpw = cpw;
   L.waves = (C + cpw - 1) / cpw;
+  L.crem = L.waves;
   L.imax = bucket(cpw);
   int ph = 1;
   while (ph * 2 <= cpw && B * ph * 2 <= 16) ph *= 2;

@@ -18,8 +18,8 @@
 // of the B operand (column b = lane % 16 is batch vector b).
 //
 // One workgroup per row block (16 rows sorted by group size); its W waves
-// split the row's K/256 column chunks, wave w taking chunks
-// [w*cpw, (w+1)*cpw). Per wave:
+// split the row's K/256 column chunks into contiguous ranges, cpw chunks for
+// waves w < crem and cpw - 1 after (fewer at the end of the row). Per wave:
 //  1. loads, all issued up front and in this order: the wave's x slice
 //     (16-byte loads, cached), then codes, offsets and scale|zero words of
 //     every chunk (non-temporal: the weights are read once); lanes without
@@ -69,7 +69,8 @@ struct KParams {
   uint32_t blob_bytes;
   uint32_t off_codes, off_offs, off_perm, off_sz;
   int32_t N, K, B, C;    // C = K / 256 column chunks
-  int32_t cpw;           // column chunks per wave
+  int32_t cpw;           // column chunks per wave (at most)
+  int32_t crem;          // waves w < crem take cpw chunks, the later ones cpw - 1
   int32_t phase;         // chunks whose x slice is staged at once
   int32_t T;             // row blocks (= workgroups)
   int32_t cls_row[5];    // first sorted row of group size 32, 64, 128, 256, then N
@@ -183,8 +184,10 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
   const int B = p.B, PH = p.phase;
   const auto rbuf = make_rsrc(p.blob, p.blob_bytes);
   const auto rx = make_rsrc(p.x, (uint32_t)(B * p.K * 2));
-  const int c0 = w * p.cpw;
-  const int ncw = p.C - c0 < p.cpw ? (p.C - c0 > 0 ? p.C - c0 : 0) : p.cpw;   // chunks of this wave
+  // chunks of this wave: [c0, c0 + ncw), contiguous over the waves
+  const int c0 = w * p.cpw - (w > p.crem ? w - p.crem : 0);
+  const int cw_max = p.cpw - (w >= p.crem ? 1 : 0);
+  const int ncw = p.C - c0 < cw_max ? (p.C - c0 > 0 ? p.C - c0 : 0) : cw_max;
 
   // this lane's sorted row, its group size 32 << cls and its scale|zero words
   const int row = rb * 16 + r;
@@ -453,8 +456,10 @@ __device__ __forceinline__ void sgemv_block_rb(const KParams& p, const int rb0) 
   const int B = p.B, PH = p.phase;
   const auto rbuf = make_rsrc(p.blob, p.blob_bytes);
   const auto rx = make_rsrc(p.x, (uint32_t)(B * p.K * 2));
-  const int c0 = w * p.cpw;
-  const int ncw = p.C - c0 < p.cpw ? (p.C - c0 > 0 ? p.C - c0 : 0) : p.cpw;   // chunks of this wave
+  // chunks of this wave: [c0, c0 + ncw), contiguous over the waves
+  const int c0 = w * p.cpw - (w > p.crem ? w - p.crem : 0);
+  const int cw_max = p.cpw - (w >= p.crem ? 1 : 0);
+  const int ncw = p.C - c0 < cw_max ? (p.C - c0 > 0 ? p.C - c0 : 0) : cw_max;
 
   // 0. original index of row tid of the RB blocks (lanes tid < 16 RB)
   const uint32_t orow = tid < 16 * RB && rb0 * 16 + tid < 16 * p.T

@@ -62,6 +62,7 @@ int make_plan(const sgemv_desc* d, int32_t B, sgemv_plan_t* pl, Launch* geo) {
   q.block = 64 * L.waves;
   q.waves = L.waves;
   q.chunks_per_wave = L.cpw;
+  q.full_waves = L.crem;
   q.phase_chunks = L.phase;
   q.x_loads = L.xloads;
   *pl = q;
@@ -82,6 +83,7 @@ KParams make_params(const sgemv_desc* d, const void* blob, const void* x, void* 
   p.off_sz = (uint32_t)d->off_sz;
   p.N = d->N; p.K = d->K; p.B = B; p.C = d->chunks;
   p.cpw = L.cpw;
+  p.crem = L.crem;
   p.phase = L.phase;
   p.T = d->n_blocks;
   p.cls_row[0] = 0;
@@ -120,6 +122,7 @@ int make_group_plan(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_pla
   q.block = 64 * L.waves;
   q.waves = L.waves;
   q.chunks_per_wave = L.cpw;
+  q.full_waves = L.crem;
   q.phase_chunks = L.phase;
   q.x_loads = L.xloads;
   *pl = q;

@@ -50,7 +50,7 @@ class Plan(ctypes.Structure):
     _fields_ = [
         ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int64), ("block", ctypes.c_int32),
         ("waves", ctypes.c_int32), ("chunks_per_wave", ctypes.c_int32), ("phase_chunks", ctypes.c_int32),
-        ("x_loads", ctypes.c_int32), ("row_blocks", ctypes.c_int32),
+        ("x_loads", ctypes.c_int32), ("row_blocks", ctypes.c_int32), ("full_waves", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:

@@ -168,11 +168,51 @@ def test_error_paths():
         sg.layout(bad, canon)
 
 
+def wave_chunks(pl, C):
+    """Chunk range [c0, c0 + n) of every wave of a plan: chunks_per_wave for
+    the first full_waves waves, one less after, contiguous, clipped to C."""
+    out = []
+    for w in range(pl.waves):
+        c0 = w * pl.chunks_per_wave - max(0, w - pl.full_waves)
+        n = pl.chunks_per_wave - (1 if w >= pl.full_waves else 0)
+        out.append((c0, max(0, min(n, C - c0))))
+    return out
+
+
+def covers_exactly(pl, C):
+    """The waves' ranges tile the C chunks in order, none left over."""
+    assert 1 <= pl.full_waves <= pl.waves
+    nxt = 0
+    for c0, n in wave_chunks(pl, C):
+        assert c0 == nxt or n == 0
+        nxt = c0 + n if n else nxt
+    assert nxt == C
+    # the last wave has work, unless a wider layer set the geometry
+    return wave_chunks(pl, C)[-1][1] > 0
+
+
+def test_balanced_split_of_the_11008_column_layer():
+    """K = 11008 (43 chunks) at one vector: 12 waves, 7 of 4 chunks and 5
+    of 3, so that no SIMD of the workgroup (wave w on SIMD w % 4) holds more
+    than 11 chunks; 11 waves of 4 would put 12 on one."""
+    d = sg.describe(4096, 11008, 1, np.full(4096, 128, np.int32))
+    pl = sg.plan(d, 1)
+    assert (pl.waves, pl.chunks_per_wave, pl.full_waves) == (12, 4, 7)
+    per = [0, 0, 0, 0]
+    for w, (c0, n) in enumerate(wave_chunks(pl, 43)):
+        per[w % 4] += n
+    assert max(per) == 11 and sum(per) == 43
+    # 4096 columns (16 chunks): 8 waves of 2, already even
+    d = sg.describe(11008, 4096, 2, np.full(11008, 128, np.int32))
+    pl = sg.plan(d, 1)
+    assert (pl.waves, pl.chunks_per_wave, pl.full_waves) == (8, 2, 8)
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_launch_plan_covers_every_chunk_once(seed):
     """sgemv_plan (host arithmetic only): one workgroup per row_blocks row
     blocks (1, or 4 for 8+ vectors on INT4 sparse layers with K <= 4096 and
-    640+ row blocks); its waves split the column chunks in whole slices; x
+    640+ row blocks); its waves split the column chunks in contiguous ranges; x
     phases fit the 8 loads per lane, the weights of row_blocks x
     chunks_per_wave pieces fit the register budget, and the LDS holds every
     wave's slice plus the partial sums."""
@@ -195,7 +235,7 @@ def test_launch_plan_covers_every_chunk_once(seed):
             assert 1 <= pl.chunks_per_wave <= 8
             imax = 1 << (pl.chunks_per_wave - 1).bit_length()
             assert rb * imax <= 8
-            assert (pl.waves - 1) * pl.chunks_per_wave < C <= pl.waves * pl.chunks_per_wave
+            assert covers_exactly(pl, C)
             assert 1 <= pl.phase_chunks <= pl.chunks_per_wave
             assert pl.phase_chunks & (pl.phase_chunks - 1) == 0          # a power of two
             assert pl.x_loads == -(-(B * pl.phase_chunks * 32) // 64) and pl.x_loads <= 8
@@ -267,7 +307,9 @@ def test_group_plan_and_host_errors():
                 cmax = max(d.chunks for d in ds)
                 assert pl.grid == sum(d.n_blocks for d in ds)
                 assert pl.block == 64 * pl.waves and 1 <= pl.waves <= 16
-                assert (pl.waves - 1) * pl.chunks_per_wave < cmax <= pl.waves * pl.chunks_per_wave
+                assert covers_exactly(pl, cmax)
+                for d in ds:                      # narrower layers: a prefix, the rest idle
+                    covers_exactly(pl, d.chunks)
                 assert pl.lds_bytes == pl.waves * B * (pl.phase_chunks * 512 + 16) + B * 16 * 16 * 4
             # a group of one is planned like the single call
             # (the single call may merge row blocks; the group launch does not)
