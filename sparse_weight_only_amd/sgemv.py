@@ -303,11 +303,18 @@ class SparseGemvLayer:
         import torch
         squeeze = x.dim() == 1
         x2 = x.reshape(1, -1) if squeeze else x
-        if x2.dtype != torch.float16 or not x2.is_contiguous() or x2.shape[1] != self.desc.K:
-            raise ValueError("x must be a contiguous FP16 tensor with K columns")
+        if x2.dim() != 2 or x2.dtype != torch.float16 or not x2.is_contiguous() or x2.shape[1] != self.desc.K:
+            raise ValueError("x must be a contiguous FP16 tensor of shape [K] or [B, K]")
+        if x2.device != self.blob.device:
+            raise ValueError(f"x is on {x2.device}, the layer on {self.blob.device}")
         B = x2.shape[0]
         if y is None:
             y = torch.empty((B, self.desc.N), dtype=torch.float16, device=x.device)
+        elif (y.dtype != torch.float16 or not y.is_contiguous() or y.device != self.blob.device
+              or y.numel() != B * self.desc.N):
+            # the kernel writes B * N FP16 values at y's address: anything else
+            # would be written past the end of a smaller buffer
+            raise ValueError(f"y must be a contiguous FP16 tensor of {B * self.desc.N} elements on {self.blob.device}")
         s = stream if stream is not None else torch.cuda.current_stream(x.device)
         run(self.desc, self.blob.data_ptr(), x2.data_ptr(), y.data_ptr(), B, s.cuda_stream)
         return y.reshape(-1) if squeeze else y

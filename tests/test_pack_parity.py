@@ -464,3 +464,36 @@ def test_fp16_form_errors():
     with pytest.raises(sg.SgemvError) as e:
         sg.plan_group(fake, 1)
     assert e.value.code == E.SGEMV_EINVAL
+
+
+def test_layer_run_rejects_bad_buffers_before_any_launch():
+    """SparseGemvLayer.run checks x and y on the host: a y smaller than B x N,
+    of another dtype or not contiguous, an x of the wrong width or dtype, or
+    tensors on another device than the layer raise before sg.run is called
+    (the layer is built on the CPU here, so a launch would be an error too)."""
+    import torch
+    rng = np.random.default_rng(5)
+    W = (rng.standard_normal((40, 512)) * 0.02).astype(np.float16)
+    gs = np.full(40, 128, np.int32)
+    canon = sg.pack(W, 2, gs)
+    d = sg.describe(40, 512, 2, gs)
+    # a host-resident layer (the constructor's device-alignment check is for
+    # device blobs, so the attributes are set directly)
+    layer = object.__new__(sg.SparseGemvLayer)
+    layer.desc, layer.canon, layer.blob_host = d, canon, sg.layout(d, canon)
+    layer.blob = torch.from_numpy(layer.blob_host)
+    x = torch.zeros((3, 512), dtype=torch.float16)
+    bad = [
+        dict(x=torch.zeros((3, 256), dtype=torch.float16)),                  # wrong K
+        dict(x=torch.zeros((3, 512), dtype=torch.float32)),                  # wrong dtype
+        dict(x=torch.zeros((512, 3), dtype=torch.float16).t()),              # not contiguous
+        dict(x=x, y=torch.empty((2, 40), dtype=torch.float16)),              # y too small
+        dict(x=x, y=torch.empty((3, 40), dtype=torch.float32)),              # y of another dtype
+        dict(x=x, y=torch.empty((40, 3), dtype=torch.float16).t()),          # y not contiguous
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            layer.run(kw["x"], kw.get("y"))
+    if torch.cuda.is_available():
+        with pytest.raises(ValueError):
+            layer.run(x.cuda())                                               # x on another device
