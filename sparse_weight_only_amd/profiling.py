@@ -5,6 +5,7 @@ Usage (after the rocprofv3 runs named in each summary's header):
     python -m sparse_weight_only_amd.profiling stats  <kernel_stats.csv> <out.txt> "<command>" [<kernel_trace.csv>]
     python -m sparse_weight_only_amd.profiling traffic <fetch counter_collection.csv>
                      <write counter_collection.csv> <out.json> "<fetch command>" "<write command>"
+    python -m sparse_weight_only_amd.profiling counters <out.txt> <counter_collection.csv>... -- "<command>"...
 
 ``traffic`` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the
 same counters read for the 64 MiB reference copy that ``bench.py`` performs
@@ -132,9 +133,37 @@ def _bench_layer_kernels() -> dict:
     return res
 
 
+def counters_summary(csvs, out_txt: str, commands, min_calls: int = 20) -> None:
+    """Median of every counter per launch shape (kernel, grid, workgroup) over
+    one or more --pmc runs; shapes with fewer than min_calls dispatches are
+    left out. Values are per dispatch, summed over the chip as rocprofv3
+    reports them."""
+    by = defaultdict(lambda: defaultdict(list))
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+            by[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for v in by.values() for c in v})
+    lines = [f"# rocprofv3 counters per dispatch, median per launch shape (kernel sources {kernel_source_hash()})"]
+    lines += [f"# command: {c}" for c in commands]
+    lines += ["", f"{'kernel':34s} {'grid':>7s} {'wg':>5s} {'calls':>6s}  " + "  ".join(f"{n:>26s}" for n in names)]
+    for (name, grid, wg), v in sorted(by.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        calls = max(len(x) for x in v.values())
+        if calls < min_calls:
+            continue
+        vals = "  ".join(f"{statistics.median(v[n]):26.1f}" if n in v else f"{'-':>26s}" for n in names)
+        lines.append(f"{name[:34]:34s} {grid:7d} {wg:5d} {calls:6d}  {vals}")
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 5 and sys.argv[1] == "stats":
         stats_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5] if len(sys.argv) > 5 else None)
+    elif len(sys.argv) >= 4 and sys.argv[1] == "counters":
+        # counters <out.txt> <csv>... -- <command>...
+        sep = sys.argv.index("--")
+        counters_summary(sys.argv[3:sep], sys.argv[2], sys.argv[sep + 1:])
     elif len(sys.argv) >= 7 and sys.argv[1] == "traffic":
         print(json.dumps(traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6],
                                          _bench_layer_kernels()), indent=1))
