@@ -45,8 +45,9 @@ Beside the step, the same line reports
   bytes depend only on the shape, the N:M choice and the number of rows per
   group size, which the adaptive policy fixes at ceil(N/10) fine rows.
 
-Prints one JSON line. ``--gpus N`` with N > 1 is refused: this build runs on
-one GPU.
+Prints one JSON line. ``--gpus N`` with N > 1 is refused: the benchmark
+measures one GPU (a multi-GPU layer would shard by output rows, each GPU
+running this same kernel on its share).
 """
 import argparse
 import json
@@ -131,8 +132,9 @@ def cpu_baseline(layers_host):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the path would shard by output rows; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(a multi-GPU layer would shard by output rows, each GPU running the same kernel "
+              "on its share)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
