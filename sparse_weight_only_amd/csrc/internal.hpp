@@ -105,11 +105,13 @@ inline Launch launch_geometry(int C, int T, int B) {
   // smaller slices when the layer has few row blocks, so the grid has
   // enough waves to cover the chip (256 CUs x 4 SIMDs, two waves each)
   while (cpw > 1 && (int64_t)T * ((C + cpw - 1) / cpw) < 2048) cpw /= 2;
-  // one step further below 4096 waves, where the workgroup stays within 16
-  // waves: 4096 x 4096 layers (256 row blocks) as 16 waves of one chunk took
-  // 3.62-3.64 us per call against 3.73-3.75 us as 8 waves of two, and the
-  // 224-GEMV decoder sequence 961 us against 974 us
-  if (cpw > 1 && (int64_t)T * ((C + cpw - 1) / cpw) < 4096 && (C + cpw / 2 - 1) / (cpw / 2) <= kMaxWaves) cpw /= 2;
+  // one vector: one step further below 4096 waves, where the workgroup
+  // stays within 16 waves: 4096 x 4096 layers (256 row blocks) as 16 waves
+  // of one chunk took 3.62-3.64 us per call against 3.73-3.75 us as 8 waves
+  // of two, and the 224-GEMV decoder sequence 961 us against 974 us (several
+  // vectors keep the previous geometry: not measured)
+  if (B == 1 && cpw > 1 && (int64_t)T * ((C + cpw - 1) / cpw) < 4096 && (C + cpw / 2 - 1) / (cpw / 2) <= kMaxWaves)
+    cpw /= 2;
   if ((C + cpw - 1) / cpw > kMaxWaves) cpw = (C + kMaxWaves - 1) / kMaxWaves;
   L.cpw = cpw;
   L.waves = (C + cpw - 1) / cpw;
