@@ -74,6 +74,7 @@ struct KParams {
   int32_t phase;         // chunks whose x slice is staged at once
   int32_t T;             // row blocks (= workgroups)
   int32_t cls_row[5];    // first sorted row of group size 32, 64, 128, 256, then N
+  int32_t cls_bias;      // 4 * cls_row[1] + 2 * cls_row[2] + cls_row[3]
 };
 
 // Raw buffer loads: 32-bit lane offsets from a per-workgroup base held in
@@ -146,17 +147,24 @@ __device__ __forceinline__ uint32_t deq_hi(uint32_t w, uint32_t magic, const Deq
 }
 
 // Number of scale|zero words per column chunk of the sorted rows before row
-// i: sum over classes k of (256 / (32 << k)) * (rows of class k before i).
+// i (0 <= i <= N): sum over classes k of (8 >> k) * (rows of class k before
+// i), the rows of class k before i being min(max(i, c_k), c_{k+1}) - c_k
+// (c = cls_row, ascending). The constant parts sum to cls_bias; the weighted
+// sum of the clamps is three shift-and-adds on the scalar unit.
 __device__ __forceinline__ int words_before(const KParams& p, int i) {
-  int s = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    int n = i - p.cls_row[k];
-    n = n < 0 ? 0 : n;
-    const int nk = p.cls_row[k + 1] - p.cls_row[k];
-    s += (8 >> k) * (n < nk ? n : nk);
-  }
-  return s;
+  const int m0 = min(i, p.cls_row[1]);
+  const int m1 = min(max(i, p.cls_row[1]), p.cls_row[2]);
+  const int m2 = min(max(i, p.cls_row[2]), p.cls_row[3]);
+  const int m3 = min(max(i, p.cls_row[3]), p.cls_row[4]);
+  return (m0 << 3) + (m1 << 2) + (m2 << 1) + m3 - p.cls_bias;
+}
+
+// Class (0..3) of sorted row i: the number of class starts c_1..c_3 at or
+// before it, each test as the sign bit of c_k - 1 - i (integer arithmetic
+// the scalar unit keeps for a wave-uniform i).
+__device__ __forceinline__ int class_of(const KParams& p, int i) {
+  return (int)(((uint32_t)(p.cls_row[1] - 1 - i) >> 31) + ((uint32_t)(p.cls_row[2] - 1 - i) >> 31) +
+               ((uint32_t)(p.cls_row[3] - 1 - i) >> 31));
 }
 
 typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
@@ -197,7 +205,7 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
   const uint32_t rec_words = (uint32_t)(words_before(p, rb * 16 + 16) - wb0);
   // a block whose 16 rows share one group size (all but at most three blocks
   // of a layer) holds 256/g words per row, row after row
-  const int cls_first = (rb * 16 >= p.cls_row[1]) + (rb * 16 >= p.cls_row[2]) + (rb * 16 >= p.cls_row[3]);
+  const int cls_first = class_of(p, rb * 16);
   const bool one_class = rec_words == (uint32_t)(16 * (8 >> cls_first));
   const uint32_t sz_row = one_class ? (uint32_t)(r * (8 >> cls_first)) : (uint32_t)(words_before(p, row) - wb0);
   const uint32_t sz_lane = sz_row + (uint32_t)((64 * q) >> glog);
@@ -499,7 +507,7 @@ __device__ __forceinline__ void sgemv_block_rb(const KParams& p, const int rb0) 
     const int cls = (row >= p.cls_row[1]) + (row >= p.cls_row[2]) + (row >= p.cls_row[3]);
     const int wb0 = words_before(p, rb * 16);
     const uint32_t rec_words = (uint32_t)(words_before(p, rb * 16 + 16) - wb0);
-    const int cls_first = (rb * 16 >= p.cls_row[1]) + (rb * 16 >= p.cls_row[2]) + (rb * 16 >= p.cls_row[3]);
+    const int cls_first = class_of(p, rb * 16);
     const bool one_class = rec_words == (uint32_t)(16 * (8 >> cls_first));
     const uint32_t sz_row = one_class ? (uint32_t)(r * (8 >> cls_first)) : (uint32_t)(words_before(p, row) - wb0);
     const uint32_t sz_lane = sz_row + (uint32_t)((64 * q) >> (5 + cls));
