@@ -303,8 +303,13 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
   constexpr bool slot_major = ONE;
   float* part = reinterpret_cast<float*>(smem + W * B * xrow_units * 16);
   if constexpr (slot_major) {
-    for (int e = tid; e < 16 * B * 16; e += blockDim.x)   // (batch row, row, slot)
-      if ((e & 15) >= W) part[e] = 0.f;
+    // 256 entries (row, slot): one pass when the workgroup has 4+ waves
+    if (W >= 4) {
+      if (tid < 256 && (tid & 15) >= W) part[tid] = 0.f;
+    } else {
+      for (int e = tid; e < 256; e += blockDim.x)
+        if ((e & 15) >= W) part[e] = 0.f;
+    }
   } else {
     for (int e = tid; e < (16 - W) * B * 4; e += blockDim.x)
       reinterpret_cast<f4*>(part)[W * B * 4 + e] = f4{0.f, 0.f, 0.f, 0.f};
@@ -418,8 +423,9 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
   }
   __syncthreads();
   // entries e = 16 b + row; the block size is a multiple of 16, so every
-  // entry of this lane has row tid % 16; the waves are added in order
-  for (int e = tid; e < 16 * B; e += blockDim.x) {
+  // entry of this lane has row tid % 16; the waves are added in order (one
+  // vector: the 16 entries of lanes 0..15, no loop)
+  for (int e = tid; ONE ? e < 16 : e < 16 * B; e += ONE ? 1024 : blockDim.x) {
     float vv[16];
     if constexpr (slot_major) {
       const f4* pv = reinterpret_cast<const f4*>(part + e * 16);
