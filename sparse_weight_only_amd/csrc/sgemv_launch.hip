@@ -88,7 +88,7 @@ KParams make_params(const sgemv_desc* d, const void* blob, const void* x, void* 
   p.T = d->n_blocks;
   p.cls_row[0] = 0;
   for (int c = 0; c < 4; ++c) p.cls_row[c + 1] = p.cls_row[c] + d->class_rows[c];
-  p.cls_bias = 4 * p.cls_row[1] + 2 * p.cls_row[2] + p.cls_row[3];
+  p.waves = L.waves;
   return p;
 }
 
