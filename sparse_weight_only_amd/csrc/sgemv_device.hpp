@@ -662,18 +662,30 @@ __global__ __launch_bounds__(1024) void sgemv_f16_kernel(KParams p) {
 constexpr int kMaxGroup = 32;
 struct GParams {
   int32_t count;
-  int32_t first_block[kMaxGroup + 1];
+  int32_t first_block[kMaxGroup + 1];   // prefix of the layers' row blocks; INT32_MAX past count
   KParams t[kMaxGroup];
 };
 static_assert(sizeof(GParams) <= 4096, "kernel arguments are limited to 4 KiB");
 
+// Layer of workgroup b (the grid is exactly first_block[count] workgroups).
+// The entries past count hold INT32_MAX, so the first three boundaries are
+// tested without waiting for count: groups of up to 4 layers (those of a
+// decoder step) find their layer with one round of argument loads before
+// loading the layer's parameters; larger groups continue in a loop. Each
+// test is the sign bit of first_block[j] - 1 - b (no overflow: b >= 0).
 template <int NK, int IMAX, int XMAX, bool V16, bool ONE = false>
 __device__ __forceinline__ void group_block(const GParams& g) {
   const int b = (int)blockIdx.x;
-  if (b >= g.first_block[g.count]) return;
-  int i = 0;
-  while (i + 1 < g.count && b >= g.first_block[i + 1]) ++i;
-  sgemv_block<NK, IMAX, XMAX, V16, ONE>(g.t[i], b - g.first_block[i]);
+  const int fb1 = g.first_block[1], fb2 = g.first_block[2], fb3 = g.first_block[3];
+  const int s1 = (int)((uint32_t)(fb1 - 1 - b) >> 31), s2 = (int)((uint32_t)(fb2 - 1 - b) >> 31),
+            s3 = (int)((uint32_t)(fb3 - 1 - b) >> 31);
+  int i = s1 + s2 + s3;
+  int base = s3 ? fb3 : s2 ? fb2 : s1 ? fb1 : 0;   // first block of layer i
+  if (i == 3) {
+    while (i + 1 < g.count && b >= g.first_block[i + 1]) ++i;
+    base = g.first_block[i];
+  }
+  sgemv_block<NK, IMAX, XMAX, V16, ONE>(g.t[i], b - base);
 }
 template <int NK, int IMAX, int XMAX>
 __global__ __launch_bounds__(1024) void sgemv_b1_group_kernel(GParams g) {

@@ -172,6 +172,7 @@ extern "C" int sgemv_run_group(const sgemv_task* tasks, int32_t count, int32_t B
   GParams g;
   memset(&g, 0, sizeof g);
   g.count = count;
+  for (int j = 0; j <= kMaxGroup; ++j) g.first_block[j] = INT32_MAX;   // the kernel's layer search relies on it
   g.first_block[0] = 0;
   for (int32_t i = 0; i < count; ++i) {
     const sgemv_task& t = tasks[i];
