@@ -51,6 +51,7 @@ def build(verbose: bool = False, arch: str = "gfx950") -> str:
         o = os.path.join(bdir, s + ".o")
         jobs.append((o, [hipcc, f"--offload-arch={arch}", "-std=c++17", "-O3", "-fPIC",
                          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                         "-mllvm", "-amdgpu-kernarg-preload-count=16",
                          "-Wall", "-Wno-pass-failed", "-c", os.path.join(CSRC, s), "-o", o]))
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(max_workers=workers) as ex:

@@ -1,5 +1,6 @@
 // Kernel selection shared by the instantiation units and the launcher.
 #pragma once
+#include <stdint.h>
 
 namespace sgemv_dev {
 
@@ -26,12 +27,16 @@ inline GroupFn get_group_kernel(int nk, int imax, int xmax) {
        : nk == 4 ? get_group_kernel_nk4(imax, xmax) : nullptr;
 }
 
-// Kernels for exactly one vector (INT4 form, nk 1 or 2; xmax 1, 2 or 4).
-KernelFn get_b1_kernel_nk1(int imax, int xmax);
-KernelFn get_b1_kernel_nk2(int imax, int xmax);
+// Kernels for exactly one vector (INT4 form, nk 1 or 2; xmax 1, 2 or 4):
+// the fields needed first as leading scalar arguments (preloaded into
+// registers), then the parameter block.
+typedef void (*B1Fn)(const uint8_t*, const uint16_t*, uint32_t, uint32_t, uint32_t, uint32_t, int32_t, uint32_t,
+                     int32_t, int32_t, int32_t, int32_t, KParams);
+B1Fn get_b1_kernel_nk1(int imax, int xmax);
+B1Fn get_b1_kernel_nk2(int imax, int xmax);
 GroupFn get_b1_group_kernel_nk1(int imax, int xmax);
 GroupFn get_b1_group_kernel_nk2(int imax, int xmax);
-inline KernelFn get_b1_kernel(int nk, int imax, int xmax) {
+inline B1Fn get_b1_kernel(int nk, int imax, int xmax) {
   return nk == 2 ? get_b1_kernel_nk2(imax, xmax) : nk == 1 ? get_b1_kernel_nk1(imax, xmax) : nullptr;
 }
 inline GroupFn get_b1_group_kernel(int nk, int imax, int xmax) {

@@ -638,9 +638,38 @@ template <int NK, int IMAX, int XMAX>
 __global__ __launch_bounds__(1024) void sgemv_kernel(KParams p) {
   sgemv_block<NK, IMAX, XMAX>(p, (int)blockIdx.x);
 }
-// The same for exactly one vector (B = 1).
+// The same for exactly one vector (B = 1). The fields a wave needs before
+// its first loads come as separate leading arguments, which the hardware
+// preloads into scalar registers at wave launch (kernel-argument preloading
+// of gfx950, enabled at build time); the rest, needed only at the end, stay
+// in the parameter block and are loaded from memory. cpw, crem and phase
+// are packed one byte each.
 template <int NK, int IMAX, int XMAX>
-__global__ __launch_bounds__(1024) void sgemv_b1_kernel(KParams p) {
+__global__ __launch_bounds__(1024) void sgemv_b1_kernel(const uint8_t* blob, const uint16_t* x, uint32_t blob_bytes,
+                                                         uint32_t off_offs, uint32_t off_perm, uint32_t off_sz,
+                                                         int32_t K, uint32_t cpw_crem_phase, int32_t cls1,
+                                                         int32_t cls2, int32_t cls3, int32_t cls4, KParams rest) {
+  // 14 leading argument dwords: what the hardware can preload beside the
+  // argument pointer (the codes section starts the blob: offset 0)
+  KParams p = rest;
+  p.blob = blob;
+  p.x = x;
+  p.blob_bytes = blob_bytes;
+  p.off_codes = 0;
+  p.off_offs = off_offs;
+  p.off_perm = off_perm;
+  p.off_sz = off_sz;
+  p.K = K;
+  p.C = K >> 8;
+  p.B = 1;
+  p.cpw = (int32_t)(cpw_crem_phase & 0xFFu);
+  p.crem = (int32_t)((cpw_crem_phase >> 8) & 0xFFu);
+  p.phase = (int32_t)(cpw_crem_phase >> 16);
+  p.cls_row[0] = 0;
+  p.cls_row[1] = cls1;
+  p.cls_row[2] = cls2;
+  p.cls_row[3] = cls3;
+  p.cls_row[4] = cls4;
   sgemv_block<NK, IMAX, XMAX, false, true>(p, (int)blockIdx.x);
 }
 // Several vectors, RB row blocks per workgroup: workgroup b computes row

@@ -26,7 +26,7 @@ GroupFn group_by_xmax(int xmax) {
   }
 }
 template <int IMAX>
-KernelFn b1_by_xmax(int xmax) {
+B1Fn b1_by_xmax(int xmax) {
   switch (xmax) {
     case 1: return sgemv_b1_kernel<1, IMAX, 1>;
     case 2: return sgemv_b1_kernel<1, IMAX, 2>;
@@ -45,7 +45,7 @@ GroupFn b1_group_by_xmax(int xmax) {
 }
 }  // namespace
 
-KernelFn get_b1_kernel_nk1(int imax, int xmax) {
+B1Fn get_b1_kernel_nk1(int imax, int xmax) {
   switch (imax) {
     case 1: return b1_by_xmax<1>(xmax);
     case 2: return b1_by_xmax<2>(xmax);
