@@ -7,14 +7,18 @@ namespace sgemv_dev {
 struct KParams;
 struct GParams;
 typedef void (*KernelFn)(KParams);
+// Single-layer kernels: 14 leading scalar argument dwords (preloaded into
+// registers at wave launch), then the parameter block.
+typedef void (*LeadFn)(const uint8_t*, const uint16_t*, uint32_t, uint32_t, uint32_t, uint32_t, int32_t, uint32_t,
+                       int32_t, int32_t, int32_t, int32_t, KParams);
 typedef void (*GroupFn)(GParams);
 
 // Kernel for nk kept per 4, up to imax chunks per wave and xmax 16-byte x
 // loads per lane and phase (each in {1, 2, 4, 8}); nullptr otherwise.
-KernelFn get_kernel_nk1(int imax, int xmax);
-KernelFn get_kernel_nk2(int imax, int xmax);
-KernelFn get_kernel_nk4(int imax, int xmax);
-inline KernelFn get_kernel(int nk, int imax, int xmax) {
+LeadFn get_kernel_nk1(int imax, int xmax);
+LeadFn get_kernel_nk2(int imax, int xmax);
+LeadFn get_kernel_nk4(int imax, int xmax);
+inline LeadFn get_kernel(int nk, int imax, int xmax) {
   return nk == 2 ? get_kernel_nk2(imax, xmax) : nk == 1 ? get_kernel_nk1(imax, xmax)
        : nk == 4 ? get_kernel_nk4(imax, xmax) : nullptr;
 }
@@ -30,8 +34,7 @@ inline GroupFn get_group_kernel(int nk, int imax, int xmax) {
 // Kernels for exactly one vector (INT4 form, nk 1 or 2; xmax 1, 2 or 4):
 // the fields needed first as leading scalar arguments (preloaded into
 // registers), then the parameter block.
-typedef void (*B1Fn)(const uint8_t*, const uint16_t*, uint32_t, uint32_t, uint32_t, uint32_t, int32_t, uint32_t,
-                     int32_t, int32_t, int32_t, int32_t, KParams);
+typedef LeadFn B1Fn;
 B1Fn get_b1_kernel_nk1(int imax, int xmax);
 B1Fn get_b1_kernel_nk2(int imax, int xmax);
 GroupFn get_b1_group_kernel_nk1(int imax, int xmax);
@@ -48,7 +51,7 @@ inline GroupFn get_b1_group_kernel(int nk, int imax, int xmax) {
 KernelFn get_rb_kernel(int nk, int imax, int xmax, int rb);
 
 // The FP16-valued form (nk 1 or 2).
-KernelFn get_f16_kernel(int nk, int imax, int xmax);
+LeadFn get_f16_kernel(int nk, int imax, int xmax);
 GroupFn get_f16_group_kernel(int nk, int imax, int xmax);
 
 }  // namespace sgemv_dev

@@ -628,29 +628,18 @@ __device__ __forceinline__ void sgemv_block_rb(const KParams& p, const int rb0) 
   }
 }
 
-// One launch, one layer: workgroup b computes row block b. The launcher
-// makes the grid exactly T workgroups, so there is no bound test: testing
-// blockIdx against T would make every wave wait for that kernel argument
-// before loading the others (measured: 0.1 us per call, 0.7 us per
-// four-layer step at one vector). A workgroup past T would only read zeros
-// or bytes inside the blob and store nothing (its rows are padding).
-template <int NK, int IMAX, int XMAX>
-__global__ __launch_bounds__(1024) void sgemv_kernel(KParams p) {
-  sgemv_block<NK, IMAX, XMAX>(p, (int)blockIdx.x);
-}
-// The same for exactly one vector (B = 1). The fields a wave needs before
-// its first loads come as separate leading arguments, which the hardware
-// preloads into scalar registers at wave launch (kernel-argument preloading
-// of gfx950, enabled at build time); the rest, needed only at the end, stay
-// in the parameter block and are loaded from memory. cpw, crem and phase
-// are packed one byte each.
-template <int NK, int IMAX, int XMAX>
-__global__ __launch_bounds__(1024) void sgemv_b1_kernel(const uint8_t* blob, const uint16_t* x, uint32_t blob_bytes,
-                                                         uint32_t off_offs, uint32_t off_perm, uint32_t off_sz,
-                                                         int32_t K, uint32_t cpw_crem_phase, int32_t cls1,
-                                                         int32_t cls2, int32_t cls3, int32_t cls4, KParams rest) {
-  // 14 leading argument dwords: what the hardware can preload beside the
-  // argument pointer (the codes section starts the blob: offset 0)
+// The fields a wave needs before its first loads, passed as 14 leading
+// scalar argument dwords that gfx950 preloads into scalar registers at wave
+// launch (kernel-argument preloading, enabled at build time); the rest of the
+// parameter block, needed only at the end, is loaded from memory. cpw, crem,
+// phase and B are packed one byte each; the codes section starts the blob.
+#define SGEMV_LEAD_ARGS                                                                                 \
+  const uint8_t *blob, const uint16_t *x, uint32_t blob_bytes, uint32_t off_offs, uint32_t off_perm, \
+      uint32_t off_sz, int32_t K, uint32_t packed, int32_t cls1, int32_t cls2, int32_t cls3, int32_t cls4
+__device__ __forceinline__ KParams lead_params(const uint8_t* blob, const uint16_t* x, uint32_t blob_bytes,
+                                               uint32_t off_offs, uint32_t off_perm, uint32_t off_sz, int32_t K,
+                                               uint32_t packed, int32_t cls1, int32_t cls2, int32_t cls3,
+                                               int32_t cls4, const KParams& rest) {
   KParams p = rest;
   p.blob = blob;
   p.x = x;
@@ -661,16 +650,34 @@ __global__ __launch_bounds__(1024) void sgemv_b1_kernel(const uint8_t* blob, con
   p.off_sz = off_sz;
   p.K = K;
   p.C = K >> 8;
-  p.B = 1;
-  p.cpw = (int32_t)(cpw_crem_phase & 0xFFu);
-  p.crem = (int32_t)((cpw_crem_phase >> 8) & 0xFFu);
-  p.phase = (int32_t)(cpw_crem_phase >> 16);
+  p.cpw = (int32_t)(packed & 0xFFu);
+  p.crem = (int32_t)((packed >> 8) & 0xFFu);
+  p.phase = (int32_t)((packed >> 16) & 0xFFu);
+  p.B = (int32_t)(packed >> 24);
   p.cls_row[0] = 0;
   p.cls_row[1] = cls1;
   p.cls_row[2] = cls2;
   p.cls_row[3] = cls3;
   p.cls_row[4] = cls4;
-  sgemv_block<NK, IMAX, XMAX, false, true>(p, (int)blockIdx.x);
+  return p;
+}
+#define SGEMV_LEAD_PARAMS(rest) \
+  lead_params(blob, x, blob_bytes, off_offs, off_perm, off_sz, K, packed, cls1, cls2, cls3, cls4, rest)
+
+// One launch, one layer: workgroup b computes row block b. The launcher
+// makes the grid exactly T workgroups, so there is no bound test: testing
+// blockIdx against T would make every wave wait for that kernel argument
+// before loading the others (measured: 0.1 us per call, 0.7 us per
+// four-layer step at one vector). A workgroup past T would only read zeros
+// or bytes inside the blob and store nothing (its rows are padding).
+template <int NK, int IMAX, int XMAX>
+__global__ __launch_bounds__(1024) void sgemv_kernel(SGEMV_LEAD_ARGS, KParams rest) {
+  sgemv_block<NK, IMAX, XMAX>(SGEMV_LEAD_PARAMS(rest), (int)blockIdx.x);
+}
+// The same for exactly one vector (B = 1).
+template <int NK, int IMAX, int XMAX>
+__global__ __launch_bounds__(1024) void sgemv_b1_kernel(SGEMV_LEAD_ARGS, KParams rest) {
+  sgemv_block<NK, IMAX, XMAX, false, true>(SGEMV_LEAD_PARAMS(rest), (int)blockIdx.x);
 }
 // Several vectors, RB row blocks per workgroup: workgroup b computes row
 // blocks RB*b .. RB*b + RB - 1. At most 8 waves, so that the weights of
@@ -680,8 +687,8 @@ __global__ __launch_bounds__(512) void sgemv_rb_kernel(KParams p) {
   sgemv_block_rb<NK, IMAX, XMAX, RB>(p, (int)blockIdx.x * RB);   // grid: ceil(T / RB), no bound test
 }
 template <int NK, int IMAX, int XMAX>
-__global__ __launch_bounds__(1024) void sgemv_f16_kernel(KParams p) {
-  sgemv_block<NK, IMAX, XMAX, true>(p, (int)blockIdx.x);   // grid: T, no bound test
+__global__ __launch_bounds__(1024) void sgemv_f16_kernel(SGEMV_LEAD_ARGS, KParams rest) {
+  sgemv_block<NK, IMAX, XMAX, true>(SGEMV_LEAD_PARAMS(rest), (int)blockIdx.x);   // grid: T, no bound test
 }
 
 // One launch, several independent layers with the same N:M choice, batch and

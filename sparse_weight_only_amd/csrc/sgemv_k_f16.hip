@@ -7,7 +7,7 @@ namespace sgemv_dev {
 
 namespace {
 template <int NK, int IMAX>
-KernelFn by_xmax(int xmax) {
+LeadFn by_xmax(int xmax) {
   switch (xmax) {
     case 1: return sgemv_f16_kernel<NK, IMAX, 1>;
     case 2: return sgemv_f16_kernel<NK, IMAX, 2>;
@@ -27,7 +27,7 @@ GroupFn group_by_xmax(int xmax) {
   }
 }
 template <int NK>
-KernelFn by_imax(int imax, int xmax) {
+LeadFn by_imax(int imax, int xmax) {
   switch (imax) {
     case 1: return by_xmax<NK, 1>(xmax);
     case 2: return by_xmax<NK, 2>(xmax);
@@ -48,7 +48,7 @@ GroupFn group_by_imax(int imax, int xmax) {
 }
 }  // namespace
 
-KernelFn get_f16_kernel(int nk, int imax, int xmax) {
+LeadFn get_f16_kernel(int nk, int imax, int xmax) {
   return nk == 2 ? by_imax<2>(imax, xmax) : nk == 1 ? by_imax<1>(imax, xmax) : nullptr;
 }
 

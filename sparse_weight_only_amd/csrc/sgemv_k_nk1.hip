@@ -6,7 +6,7 @@ namespace sgemv_dev {
 
 namespace {
 template <int IMAX>
-KernelFn by_xmax(int xmax) {
+LeadFn by_xmax(int xmax) {
   switch (xmax) {
     case 1: return sgemv_kernel<1, IMAX, 1>;
     case 2: return sgemv_kernel<1, IMAX, 2>;
@@ -65,7 +65,7 @@ GroupFn get_b1_group_kernel_nk1(int imax, int xmax) {
   }
 }
 
-KernelFn get_kernel_nk1(int imax, int xmax) {
+LeadFn get_kernel_nk1(int imax, int xmax) {
   switch (imax) {
     case 1: return by_xmax<1>(xmax);
     case 2: return by_xmax<2>(xmax);

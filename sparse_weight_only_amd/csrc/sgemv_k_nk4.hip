@@ -7,7 +7,7 @@ namespace sgemv_dev {
 
 namespace {
 template <int IMAX>
-KernelFn by_xmax(int xmax) {
+LeadFn by_xmax(int xmax) {
   switch (xmax) {
     case 1: return sgemv_kernel<4, IMAX, 1>;
     case 2: return sgemv_kernel<4, IMAX, 2>;
@@ -28,7 +28,7 @@ GroupFn group_by_xmax(int xmax) {
 }
 }  // namespace
 
-KernelFn get_kernel_nk4(int imax, int xmax) {
+LeadFn get_kernel_nk4(int imax, int xmax) {
   switch (imax) {
     case 1: return by_xmax<1>(xmax);
     case 2: return by_xmax<2>(xmax);

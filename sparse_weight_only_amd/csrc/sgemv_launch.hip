@@ -146,25 +146,25 @@ extern "C" int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* 
   if (rc) return rc;
   if (!aligned(blob_dev, x_dev, y_dev)) return SGEMV_EALIGN;
   const KParams p = make_params(d, blob_dev, x_dev, y_dev, B, L);
-  if (d->value_format == 0 && L.rb == 1 && B == 1 && d->nk != 4) {
-    // one vector: the fields needed first go as leading scalar arguments,
-    // which the hardware preloads into registers
-    sgemv_dev::B1Fn f1 = sgemv_dev::get_b1_kernel(d->nk, L.imax, L.xmax);
+  if (L.rb == 1) {
+    // one layer, one row block per workgroup: the fields needed first go as
+    // leading scalar arguments, which the hardware preloads into registers
+    sgemv_dev::LeadFn f1 = d->value_format == 1       ? sgemv_dev::get_f16_kernel(d->nk, L.imax, L.xmax)
+                           : (B == 1 && d->nk != 4)   ? sgemv_dev::get_b1_kernel(d->nk, L.imax, L.xmax)
+                                                      : sgemv_dev::get_kernel(d->nk, L.imax, L.xmax);
     if (!f1 || L.cpw > 255 || L.crem > 255 || L.phase > 255 || p.off_codes != 0) return SGEMV_ESIZE;
     if (pl.lds_bytes > 65536) {
       if (hipFuncSetAttribute((const void*)f1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds_bytes) != hipSuccess)
         return SGEMV_EHIP;
     }
-    const uint32_t packed = (uint32_t)L.cpw | ((uint32_t)L.crem << 8) | ((uint32_t)L.phase << 16);
+    const uint32_t packed = (uint32_t)L.cpw | ((uint32_t)L.crem << 8) | ((uint32_t)L.phase << 16) | ((uint32_t)B << 24);
     hipLaunchKernelGGL(f1, dim3((uint32_t)pl.grid), dim3(pl.block), (uint32_t)pl.lds_bytes, (hipStream_t)hip_stream,
                        p.blob, p.x, p.blob_bytes, p.off_offs, p.off_perm, p.off_sz, p.K, packed,
                        p.cls_row[1], p.cls_row[2], p.cls_row[3], p.cls_row[4], p);
     if (hipGetLastError() != hipSuccess) return SGEMV_EHIP;
     return SGEMV_OK;
   }
-  KernelFn fn = d->value_format == 1 ? sgemv_dev::get_f16_kernel(d->nk, L.imax, L.xmax)
-              : L.rb > 1                ? sgemv_dev::get_rb_kernel(d->nk, L.imax, L.xmax, L.rb)
-                                        : sgemv_dev::get_kernel(d->nk, L.imax, L.xmax);
+  KernelFn fn = sgemv_dev::get_rb_kernel(d->nk, L.imax, L.xmax, L.rb);
   if (!fn) return SGEMV_ESIZE;
   if (pl.lds_bytes > 65536) {
     if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds_bytes) != hipSuccess)
