@@ -12,15 +12,22 @@ Timing protocol
 * cold weights: every layer has R device copies, cycled so that the bytes
   touched between two uses of one copy exceed 512 MiB (twice the 256 MB
   Infinity Cache);
-* the timed steps are captured once in a HIP graph and replayed, so host
-  dispatch cost is not measured; HIP events on the launch stream bracket the
-  replays, with a device synchronisation on both sides;
+* exactly --warmup untimed steps, then exactly --steps timed steps, each set
+  captured once in a HIP graph (so host dispatch cost is not measured) and
+  replayed once; step i runs copy i % R of every layer, the timed steps
+  continuing the cycle; HIP events on the launch stream bracket the timed
+  replay, with a device synchronisation on both sides;
 * per-layer µs/call: a graph of back-to-back launches of one layer (cycling
   its copies), timed the same way; beside it, for information only, the same
   launches on a single copy (``hot_us_per_call``: the blob stays in the
   Infinity Cache, so that figure is not an HBM rate);
-* the oracle (NumPy FP64 dequantise-then-dot) is timed on the host cores on
-  one pass over the same four layers.
+* the practical ceiling of one launch (``ceiling``): an empty kernel, and a
+  plain read of each layer's algorithmic bytes less y with one 16-byte load
+  per lane, without and with a store of y's bytes, from the same cold
+  copies and timed the same way as the layer;
+* the oracle (NumPy FP64 dequantise-then-dot, and the dot alone on the
+  pre-decoded W') is timed on the host cores on passes over the same four
+  layers.
 
 Beside the step, the same line reports
 * ``ablation``: the up and down MLP weights as a dense INT4 layer (every
@@ -79,6 +86,7 @@ def parse():
     ap.add_argument("--no-ablation", action="store_true", help="skip the dense INT4 / FP16 ablation")
     ap.add_argument("--no-small", action="store_true", help="skip the 1024x1024 and 4096x4096 layers")
     ap.add_argument("--no-hot", action="store_true", help="skip the cache-resident per-layer timing")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the empty-kernel and plain-read probes")
     return ap.parse_args()
 
 
@@ -107,29 +115,46 @@ def read_traffic(kernel_hash, layer_name):
 
 
 def cpu_baseline(layers_host):
-    """The oracle, as it stands, on the host cores: decode + FP64 dot per layer."""
+    """The oracle, as it stands, on the host cores: (i) decode the 2bit-CSR
+    arrays to a dense FP64 W' and np.dot, per layer; (ii) np.dot alone on the
+    pre-decoded W'. One pass over the four layers is one sample; the median
+    of 3 (i) and 5 (ii) passes is reported."""
     import numpy as np
     from oracle import gemv as ogemv
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in pools] + [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in pools})) or "unknown"
     except Exception:
-        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    total_bytes = 0
-    times = []
+        threads, blas = int(os.environ.get("OMP_NUM_THREADS", "1")), "unknown"
+    total_bytes = sum(nb for (_, _, _, nb) in layers_host)
+    t_dec = []
     for rep in range(3):
         t0 = time.perf_counter()
         for (name, canon, X, nbytes) in layers_host:
             Wd = ogemv.dequant_dense(canon)
             ogemv.gemv(Wd, X)
             del Wd
-            if rep == 0:
-                total_bytes += nbytes
-        times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
-    return {"value": round(total_bytes / t / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": "one pass over the 4 MLP layers (decode 2bit-CSR to dense FP64, then np.dot), "
-                      f"median of 3 passes, {t:.2f} s per pass"}
+        t_dec.append(time.perf_counter() - t0)
+    dense = [(ogemv.dequant_dense(canon), X) for (_, canon, X, _) in layers_host]
+    t_dot = []
+    for rep in range(6):
+        t0 = time.perf_counter()
+        for Wd, X in dense:
+            ogemv.gemv(Wd, X)
+        if rep:                                   # the first pass warms up
+            t_dot.append(time.perf_counter() - t0)
+    del dense
+    td, tt = statistics.median(t_dec), statistics.median(t_dot)
+    return {"value": round(total_bytes / td / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "one pass over the 4 MLP layers: decode 2bit-CSR to dense FP64 W', then np.dot; "
+                      f"median of 3 passes, {td:.2f} s per pass",
+            "dot_only": {"value": round(total_bytes / tt / 1e9, 4), "unit": "GB/s",
+                         "sample": f"np.dot on the pre-decoded FP64 W' of the 4 layers, median of 5 passes, "
+                                   f"{tt * 1e3:.1f} ms per pass"},
+            "affinity_cores": affinity, "blas": blas}
 
 
 def main():
@@ -182,11 +207,37 @@ def main():
         host = torch.from_numpy(l["blob_host"])
         l["copies"] = [host.to(dev) for _ in range(l["R"])]
     torch.cuda.synchronize()
-    S = max(l["R"] for l in L_dev)
     log(f"packed 4 layers in {t_pack:.1f} s; cold copies per layer: {[l['R'] for l in L_dev]}")
 
-    # ---- whole step: graph of R steps (every copy once), replayed
+    # ---- timing helpers: a body of launches captured once in a HIP graph
+    # (eager warm-up on the capture stream first), replayed on the current
+    # stream between HIP events, with a device synchronisation either side
+    def capture(body, eager_first=True):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream(dev)
+        s.wait_stream(stream)
+        if eager_first:
+            with torch.cuda.stream(s):
+                body()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            body()
+        torch.cuda.synchronize()
+        return g
+
+    def replay_ms(g, reps):
+        cur = torch.cuda.current_stream(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(cur)
+        for r in range(reps):
+            g.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
     def timed(fn_graph_body, n_body, reps, warm):
+        """ms per launch of a body of n_body launches, replayed reps times after warm replays."""
         if args.eager:
             for w in range(warm):
                 fn_graph_body()
@@ -198,39 +249,48 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / (reps * n_body)
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream(dev)
-        s.wait_stream(stream)
-        with torch.cuda.stream(s):
-            fn_graph_body()                      # eager warm-up on the capture stream
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=s):
-            fn_graph_body()
-        torch.cuda.synchronize()
+        g = capture(fn_graph_body)
         for w in range(warm):
             g.replay()
+        return replay_ms(g, reps) / (reps * n_body)
+
+    # ---- whole step, exactly --warmup untimed then --steps timed steps; step
+    # i runs copy i % R of every layer, the timed steps continuing the cycle
+    # where the warm-up left it (the bytes between two uses of a copy stay
+    # above 512 MiB, so every step is cold)
+    def steps_body(first, count):
+        def body():
+            cur = torch.cuda.current_stream(dev)
+            for i in range(first, first + count):
+                for l in L_dev:
+                    sg.run(l["desc"], l["copies"][i % l["R"]].data_ptr(), l["x"].data_ptr(), l["y"].data_ptr(), 1,
+                           cur.cuda_stream)
+        return body
+
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
+    if args.eager:
+        steps_body(0, args.warmup)()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        cur = torch.cuda.current_stream(dev)
-        e0.record(cur)
-        for r in range(reps):
-            g.replay()
-        e1.record(cur)
+        e0.record(stream)
+        steps_body(args.warmup, args.steps)()
+        e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * n_body)
-
-    reps = max(1, -(-args.steps // S))
-    warm = max(1, -(-args.warmup // S))
-
-    def body_steps():
-        cur = torch.cuda.current_stream(dev)
-        for i in range(S):
-            for l in L_dev:
-                sg.run(l["desc"], l["copies"][i % l["R"]].data_ptr(), l["x"].data_ptr(), l["y"].data_ptr(), 1,
-                       cur.cuda_stream)
-
-    ms_per_step = timed(body_steps, S, reps, warm)
-    steps = reps * S
+        ms_total = e0.elapsed_time(e1)
+    else:
+        # each layer's kernel launched once before capture (code-object
+        # loading), not a step: the step graphs themselves are not run eagerly
+        for l in L_dev:
+            sg.run(l["desc"], l["copies"][0].data_ptr(), l["x"].data_ptr(), l["y"].data_ptr(), 1, stream.cuda_stream)
+        torch.cuda.synchronize()
+        g_timed = capture(steps_body(args.warmup, args.steps), eager_first=False)
+        if args.warmup:
+            g_warm = capture(steps_body(0, args.warmup), eager_first=False)
+            g_warm.replay()
+        ms_total = replay_ms(g_timed, 1)
+    ms_per_step = ms_total / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # ---- per layer: back-to-back launches of one layer, cycling its copies
@@ -263,13 +323,54 @@ def main():
                                   "pct_hbm_peak": round(100 * l["bytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
                                   "hot_us_per_call": None if us_hot is None else round(us_hot, 3),
                                   "grid": pl.grid, "waves": pl.waves, "chunks_per_wave": pl.chunks_per_wave}
+
+    # ---- the practical ceiling of one launch, timed the same way: an empty
+    # kernel, and a plain 16-byte-per-lane read of the layer's algorithmic
+    # bytes less y (from the same cold copies), without and with a store of
+    # y's bytes
+    ceiling = None
+    if not args.no_ceiling:
+        dst = torch.empty(max(l["L"].N for l in L_dev) * 2 + 64, dtype=torch.uint8, device=dev)
+
+        def body_empty(n=400):
+            cur = torch.cuda.current_stream(dev)
+            for i in range(n):
+                sg.probe_empty(1, 64, cur.cuda_stream)
+
+        ceiling = {"empty_us": round(timed(body_empty, 400, 4, 1) * 1e3, 3), "layers": {}}
+        for l in L_dev:
+            n_copies = l["R"]
+            n = n_copies * max(1, args.layer_calls // (n_copies * 4))
+            y_bytes = 2 * l["L"].N
+            rd = (l["bytes"] - y_bytes) // 16 * 16
+            res = {"read_bytes": rd, "store_bytes": y_bytes}
+            for key, st in (("read_us", 0), ("read_store_us", y_bytes)):
+                def body_probe(l=l, n=n, st=st):
+                    cur = torch.cuda.current_stream(dev)
+                    for i in range(n):
+                        sg.probe_read(l["copies"][i % n_copies].data_ptr(), rd, dst.data_ptr(), st,
+                                      stream=cur.cuda_stream)
+                res[key] = round(timed(body_probe, n, 4, 1) * 1e3, 3)
+            pl_us = per_layer[l["L"].name]["us_per_call"]
+            res["kernel_us"] = pl_us
+            res["kernel_over_read_store"] = round(pl_us / res["read_store_us"], 3)
+            res["read_store_pct_hbm_peak"] = round(100 * l["bytes"] / (res["read_store_us"] * 1e-6) / 1e9
+                                                   / HBM_PEAK_GBS, 2)
+            ceiling["layers"][l["L"].name] = res
+        del dst
+        log("ceiling probes timed")
+
     # dominant kernel: the layer with the largest time per step
     dom = max(per_layer, key=lambda k: per_layer[k]["us_per_call"])
     d = per_layer[dom]
     khash = kernel_source_hash()
     roofline = {"bound": "hbm", "achieved": d["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(d["GBps"] / HBM_PEAK_GBS, 4), "traffic": read_traffic(khash, dom),
-                "kernel": dom, "bytes_per_launch": d["bytes"], "us_per_launch": d["us_per_call"]}
+                "kernel": dom, "bytes_per_launch": d["bytes"], "us_per_launch": d["us_per_call"],
+                "timing": "HIP events around a graph of back-to-back launches cycling cold copies, per launch"}
+    if ceiling is not None:
+        c = ceiling["layers"][dom]
+        roofline["frac_of_read_store_ceiling"] = round(c["read_store_us"] / d["us_per_call"], 4)
 
     def per_call_us(desc, copies, x, y, B, n_calls):
         n_copies = len(copies)
@@ -454,8 +555,8 @@ def main():
         log("decoder sequence timed")
 
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
-        "warmup": warm * S, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int4*f16->f32", "data": "synthetic",
         "config": {"workload": "cfg3: LLaMA-7B MLP up 4096->11008 and down 11008->4096, each at 1:4 and 2:4, "
                                "adaptive INT4 groups (ceil(N/10) rows g32, rest g128), FP16 x, batch 1",
@@ -465,6 +566,7 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "per_layer": per_layer,
         "roofline": roofline,
+        "ceiling": ceiling,
         "kernel_source_hash": khash,
         "pack_seconds": round(t_pack, 2),
     }

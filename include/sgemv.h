@@ -20,8 +20,10 @@
  *  - Every function returns an int status: SGEMV_OK (0) or a negative error
  *    code. Nothing aborts, throws or prints. All checks except SGEMV_EHIP
  *    happen on the host before any HIP call.
- *  - The library allocates no memory visible to the caller, keeps no global
- *    state and is re-entrant. Host arrays are owned and sized by the caller;
+ *  - The library allocates no memory visible to the caller and is
+ *    re-entrant. Its only state is a record of the kernels whose LDS limit
+ *    it has raised on a device (HIP keeps that attribute per kernel and
+ *    device, so it is set once), guarded by a mutex. Host arrays are owned and sized by the caller;
  *    device buffers are owned by the caller (e.g. torch tensors).
  */
 #ifndef SGEMV_H
@@ -262,6 +264,40 @@ int sgemv_plan_group(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_pl
 
 /* sgemv_strerror - static description of a status code (never NULL). */
 const char* sgemv_strerror(int code);
+
+/* sgemv_f64_to_f16 - the packer's FP64 -> FP16 conversion, exported so that
+ * callers (and tests) can reproduce the FP16 scales it stores (P1 §1 "our
+ * core idea": FP16 -> INT4 compression with FP16 group scales). Round to
+ * nearest, ties to even, in one step from binary64 (no intermediate FP32
+ * rounding); overflow gives +-inf, values below half the smallest subnormal
+ * give +-0, NaN gives the quiet NaN 0x7E00 with the input's sign.
+ *   in  : host double[n];  out : host uint16_t[n] (FP16 bit patterns).
+ * Errors: EINVAL (NULL with n > 0, n < 0). */
+int sgemv_f64_to_f16(const double* in, uint16_t* out, int64_t n);
+
+/* Measurement probes: the practical ceiling of one launch on this GPU, for
+ * comparing sgemv_run with the cost of merely launching a kernel and of
+ * merely streaming the same bytes (the pages locate the decode bottleneck
+ * in weight loading: page "高效推理论文精选", section "推理瓶颈分析",
+ * inference-bottleneck analysis). They compute nothing of the method.
+ *
+ * sgemv_probe_read - one kernel that reads `bytes` bytes at src_dev with one
+ * 16-byte non-temporal load per lane (256 lanes per workgroup, grid
+ * ceil(bytes / 4096)), folds each lane's 16 bytes into 4, and writes the
+ * folded words of the first store_bytes / 4 lanes to dst_dev (the store of
+ * a GEMV's y). Other lanes store only if their folded word equals `magic`,
+ * which keeps every load live (pass a value the data is unlikely to hold;
+ * such a lane writes dst_dev[0]).
+ *   src_dev : device, 256-byte aligned; bytes % 16 == 0, 16 <= bytes < 2^31.
+ *   dst_dev : device, 4-byte aligned, at least max(store_bytes, 4) bytes;
+ *             0 <= store_bytes <= bytes / 4, store_bytes % 4 == 0.
+ * sgemv_probe_empty - one kernel of `grid` workgroups of `block` lanes
+ * (1..1024, a multiple of 64) whose body is empty.
+ * Both enqueue on hip_stream and return without synchronising.
+ * Errors: EINVAL (arguments), EALIGN, EHIP. */
+int sgemv_probe_read(const void* src_dev, int64_t bytes, void* dst_dev, int64_t store_bytes,
+                     uint32_t magic, void* hip_stream);
+int sgemv_probe_empty(int32_t grid, int32_t block, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libsgemv.so")
 HOST_SRCS = ["host_pack.cpp", "host_layout.cpp"]
-HIP_SRCS = ["sgemv_k_nk1.hip", "sgemv_k_nk2.hip", "sgemv_k_nk4.hip", "sgemv_k_f16.hip", "sgemv_k_rb.hip", "sgemv_launch.hip"]
+HIP_SRCS = ["sgemv_k_nk1.hip", "sgemv_k_nk2.hip", "sgemv_k_nk4.hip", "sgemv_k_f16.hip", "sgemv_k_rb.hip", "sgemv_launch.hip",
+            "sgemv_probe.hip"]
 
 
 def _hipcc() -> str:
@@ -61,6 +62,8 @@ def build(verbose: bool = False, arch: str = "gfx950") -> str:
     _run([hipcc, "-shared", "-fPIC", "-o", tmp] + [o for o, _ in jobs], verbose)
     os.replace(tmp, LIB)
     build_c_driver(verbose)
+    from . import _build_san
+    _build_san.build_host_sanitized(verbose)
     return LIB
 
 

@@ -254,3 +254,9 @@ extern "C" const char* sgemv_strerror(int code) {
     default: return "unknown status code";
   }
 }
+
+extern "C" int sgemv_f64_to_f16(const double* in, uint16_t* out, int64_t n) {
+  if (n < 0 || (n > 0 && (!in || !out))) return SGEMV_EINVAL;
+  for (int64_t i = 0; i < n; ++i) out[i] = f64_to_f16(in[i]);
+  return SGEMV_OK;
+}

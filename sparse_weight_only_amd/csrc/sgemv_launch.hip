@@ -1,6 +1,10 @@
 // sgemv_plan / sgemv_run: host-side checks and the launch of the SparseGemv kernel.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "internal.hpp"
 #include "kernels.hpp"
 #include "sgemv_device.hpp"
@@ -92,6 +96,23 @@ KParams make_params(const sgemv_desc* d, const void* blob, const void* x, void* 
   return p;
 }
 
+// Dynamic LDS beyond 64 KiB needs the kernel's limit raised. The runtime
+// keeps the attribute per kernel and device, so it is set once for each
+// (kernel, device) pair, to the full 160 KiB, and remembered here.
+int ensure_lds(const void* fn, int64_t lds_bytes) {
+  if (lds_bytes <= 65536) return SGEMV_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SGEMV_EHIP;
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, int>> raised;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& e : raised)
+    if (e.first == fn && e.second == dev) return SGEMV_OK;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess) return SGEMV_EHIP;
+  raised.emplace_back(fn, dev);
+  return SGEMV_OK;
+}
+
 bool aligned(const void* blob, const void* x, const void* y) {
   return !(((uintptr_t)blob % 256) || ((uintptr_t)x % 16) || ((uintptr_t)y % 2));
 }
@@ -153,10 +174,8 @@ extern "C" int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* 
                            : (B == 1 && d->nk != 4)   ? sgemv_dev::get_b1_kernel(d->nk, L.imax, L.xmax)
                                                       : sgemv_dev::get_kernel(d->nk, L.imax, L.xmax);
     if (!f1 || L.cpw > 255 || L.crem > 255 || L.phase > 255 || p.off_codes != 0) return SGEMV_ESIZE;
-    if (pl.lds_bytes > 65536) {
-      if (hipFuncSetAttribute((const void*)f1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds_bytes) != hipSuccess)
-        return SGEMV_EHIP;
-    }
+    (void)hipGetLastError();   // a stale error of an earlier call must not be reported as this launch's
+    if (ensure_lds((const void*)f1, pl.lds_bytes)) return SGEMV_EHIP;
     const uint32_t packed = (uint32_t)L.cpw | ((uint32_t)L.crem << 8) | ((uint32_t)L.phase << 16) | ((uint32_t)B << 24);
     hipLaunchKernelGGL(f1, dim3((uint32_t)pl.grid), dim3(pl.block), (uint32_t)pl.lds_bytes, (hipStream_t)hip_stream,
                        p.blob, p.x, p.blob_bytes, p.off_offs, p.off_perm, p.off_sz, p.K, packed,
@@ -166,10 +185,8 @@ extern "C" int sgemv_run(const sgemv_desc* d, const void* blob_dev, const void* 
   }
   KernelFn fn = sgemv_dev::get_rb_kernel(d->nk, L.imax, L.xmax, L.rb);
   if (!fn) return SGEMV_ESIZE;
-  if (pl.lds_bytes > 65536) {
-    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds_bytes) != hipSuccess)
-      return SGEMV_EHIP;
-  }
+  (void)hipGetLastError();
+  if (ensure_lds((const void*)fn, pl.lds_bytes)) return SGEMV_EHIP;
   hipLaunchKernelGGL(fn, dim3((uint32_t)pl.grid), dim3(pl.block), (uint32_t)pl.lds_bytes, (hipStream_t)hip_stream, p);
   if (hipGetLastError() != hipSuccess) return SGEMV_EHIP;
   return SGEMV_OK;
@@ -201,10 +218,8 @@ extern "C" int sgemv_run_group(const sgemv_task* tasks, int32_t count, int32_t B
               : (B == 1 && nk0 != 4)             ? sgemv_dev::get_b1_group_kernel(nk0, L.imax, L.xmax)
                                                  : sgemv_dev::get_group_kernel(nk0, L.imax, L.xmax);
   if (!fn) return SGEMV_ESIZE;
-  if (pl.lds_bytes > 65536) {
-    if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds_bytes) != hipSuccess)
-      return SGEMV_EHIP;
-  }
+  (void)hipGetLastError();
+  if (ensure_lds((const void*)fn, pl.lds_bytes)) return SGEMV_EHIP;
   hipLaunchKernelGGL(fn, dim3((uint32_t)pl.grid), dim3(pl.block), (uint32_t)pl.lds_bytes, (hipStream_t)hip_stream, g);
   if (hipGetLastError() != hipSuccess) return SGEMV_EHIP;
   return SGEMV_OK;

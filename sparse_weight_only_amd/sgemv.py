@@ -19,7 +19,9 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "_lib", "libsgemv.so")
+# SGEMV_LIB may name another build of the same ABI (the tests load a
+# host-only build with address and undefined-behaviour sanitizers this way)
+_LIB_PATH = os.environ.get("SGEMV_LIB") or os.path.join(_HERE, "_lib", "libsgemv.so")
 _lib = None
 
 SGEMV_OK, SGEMV_EINVAL, SGEMV_ESIZE, SGEMV_EALIGN, SGEMV_EHIP = 0, -1, -2, -3, -4
@@ -79,25 +81,35 @@ def lib():
                                "(run __graft_entry__.build())")
         L = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
-        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
-        L.sgemv_describe.argtypes = [i32, i32, i32, P, ctypes.POINTER(Desc)]
-        L.sgemv_select_groups.argtypes = [P, i32, i32, i32, P, i32, f64, i32, i32, P]
-        L.sgemv_pack.argtypes = [P, i32, i32, i32, P, P, P, P, P, P, P]
-        L.sgemv_prune.argtypes = [P, i32, i32, i32, P, i32, P]
-        L.sgemv_describe_fp16.argtypes = [i32, i32, i32, ctypes.POINTER(Desc)]
-        L.sgemv_pack_fp16.argtypes = [P, i32, i32, i32, P, P, P]
-        L.sgemv_layout_fp16.argtypes = [ctypes.POINTER(Desc), P, P, P]
-        L.sgemv_layout.argtypes = [ctypes.POINTER(Desc), P, P, P, P, P, P]
-        L.sgemv_run.argtypes = [ctypes.POINTER(Desc), P, P, P, i32, P]
-        L.sgemv_plan.argtypes = [ctypes.POINTER(Desc), i32, ctypes.POINTER(Plan)]
-        L.sgemv_run_group.argtypes = [ctypes.POINTER(Task), i32, i32, P]
-        L.sgemv_plan_group.argtypes = [ctypes.POINTER(Task), i32, i32, ctypes.POINTER(Plan)]
+        i32, i64, u32, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_double
+        D, PL, TK = ctypes.POINTER(Desc), ctypes.POINTER(Plan), ctypes.POINTER(Task)
+        sigs = {
+            "sgemv_describe": [i32, i32, i32, P, D],
+            "sgemv_select_groups": [P, i32, i32, i32, P, i32, f64, i32, i32, P],
+            "sgemv_pack": [P, i32, i32, i32, P, P, P, P, P, P, P],
+            "sgemv_prune": [P, i32, i32, i32, P, i32, P],
+            "sgemv_describe_fp16": [i32, i32, i32, D],
+            "sgemv_pack_fp16": [P, i32, i32, i32, P, P, P],
+            "sgemv_layout_fp16": [D, P, P, P],
+            "sgemv_layout": [D, P, P, P, P, P, P],
+            "sgemv_f64_to_f16": [P, P, i64],
+            "sgemv_run": [D, P, P, P, i32, P],
+            "sgemv_plan": [D, i32, PL],
+            "sgemv_run_group": [TK, i32, i32, P],
+            "sgemv_plan_group": [TK, i32, i32, PL],
+            "sgemv_probe_read": [P, i64, P, i64, u32, P],
+            "sgemv_probe_empty": [i32, i32, P],
+        }
+        for f, argtypes in sigs.items():
+            if not hasattr(L, f):
+                # only a host-only build named by SGEMV_LIB lacks the GPU entry points
+                if "SGEMV_LIB" in os.environ:
+                    continue
+                raise RuntimeError(f"{_LIB_PATH} does not export {f}")
+            getattr(L, f).argtypes = argtypes
+            getattr(L, f).restype = ctypes.c_int
         L.sgemv_strerror.argtypes = [ctypes.c_int]
         L.sgemv_strerror.restype = ctypes.c_char_p
-        for f in ("sgemv_describe", "sgemv_select_groups", "sgemv_pack", "sgemv_prune", "sgemv_layout", "sgemv_run", "sgemv_plan",
-                  "sgemv_run_group", "sgemv_plan_group", "sgemv_describe_fp16", "sgemv_pack_fp16",
-                  "sgemv_layout_fp16"):
-            getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -136,6 +148,9 @@ def select_groups(w16: np.ndarray, nk: int, xcal16: np.ndarray, frac_fine: float
     w = _host(np.asarray(w16).view(np.uint16), np.uint16)
     xc = _host(np.asarray(xcal16).view(np.uint16), np.uint16)
     N, K = w.shape
+    if xc.ndim != 2 or xc.shape[1] != K:
+        # the library reads T x K halves at xcal's address
+        raise ValueError("xcal must be [T, K]")
     out = np.empty(N, dtype=np.int32)
     _check(lib().sgemv_select_groups(_ptr(w), N, K, nk, _ptr(xc), xc.shape[0], float(frac_fine),
                                      g_fine, g_coarse, _ptr(out)), "sgemv_select_groups")
@@ -189,6 +204,28 @@ def layout(desc: Desc, canon: dict) -> np.ndarray:
             _host(canon["gptr"], np.int32)]
     _check(lib().sgemv_layout(ctypes.byref(desc), *[_ptr(a) for a in arrs], _ptr(blob)), "sgemv_layout")
     return blob
+
+
+def f64_to_f16(x: np.ndarray) -> np.ndarray:
+    """The packer's FP64 -> FP16 conversion (round to nearest even, one step):
+    FP16 bit patterns (uint16) of the same shape."""
+    a = _host(np.asarray(x, dtype=np.float64), np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _check(lib().sgemv_f64_to_f16(_ptr(a), _ptr(out), a.size), "sgemv_f64_to_f16")
+    return out
+
+
+def probe_read(src_dev: int, nbytes: int, dst_dev: int, store_bytes: int, magic: int = 0x9E3779B9,
+               stream: int = 0) -> None:
+    """Enqueue the plain-read probe (16 bytes per lane; store_bytes written)."""
+    _check(lib().sgemv_probe_read(ctypes.c_void_p(src_dev), int(nbytes), ctypes.c_void_p(dst_dev),
+                                  int(store_bytes), int(magic) & 0xFFFFFFFF, ctypes.c_void_p(stream)),
+           "sgemv_probe_read")
+
+
+def probe_empty(grid: int = 1, block: int = 64, stream: int = 0) -> None:
+    """Enqueue the empty-kernel probe."""
+    _check(lib().sgemv_probe_empty(int(grid), int(block), ctypes.c_void_p(stream)), "sgemv_probe_empty")
 
 
 def describe_fp16(N: int, K: int, nk: int) -> Desc:

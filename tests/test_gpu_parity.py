@@ -10,7 +10,7 @@ import pytest
 import synth
 import sparse_weight_only_amd as sg
 from oracle import gemv as ogemv
-from gpu_util import TOL, say, group_sizes, make_layer, run_checked, oracle_y, check_pack_matches_oracle
+from gpu_util import TOL, say, group_sizes, make_layer, make_layer_fp16, run_checked, assert_bit_exact, Ref
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -47,19 +47,15 @@ def test_exact_arithmetic_bit_exact(nk, N, K, gs_kind):
         rows = gs == g
         W[rows] = grid_weights(int(rows.sum()), K, nk, int(g), rng)
     say(f"case exact nk={nk} N={N} K={K} groups={gs_kind}")
-    layer = make_layer(W, nk, gs)
-    co = check_pack_matches_oracle(W, nk, gs, layer.canon)
-    assert np.all(np.abs(co["scale"].view(np.float16).astype(np.float64) - 2.0 ** -6) == 0)
+    layer, ref = make_layer(W, nk, gs)
+    assert np.all(np.abs(ref.co["scale"].view(np.float16).astype(np.float64) - 2.0 ** -6) == 0)
     for B in (1, 3, 16):
         X = np.zeros((B, K), np.float16)
         for b in range(B):
             idx = rng.choice(K, size=min(64, K), replace=False)
             X[b, idx] = rng.choice([-1.0, 1.0], len(idx))
         y = run_checked(layer, X)
-        y_ref, D, _ = oracle_y(layer.canon, X)
-        want = y_ref.astype(np.float16)
-        assert np.array_equal(want.astype(np.float64), y_ref), "reference not exact"
-        assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), f"B={B}"
+        assert_bit_exact(y, ref.y(X)[0], f"B={B}")
 
 
 @pytest.mark.parametrize("L", synth.cfg1() + synth.cfg2() + synth.cfg3(), ids=lambda L: L.name)
@@ -67,8 +63,8 @@ def test_one_hot_columns_bit_exact(L):
     W = L.W()
     gs = group_sizes(L, W)
     say(f"case one-hot {L.name}")
-    layer = make_layer(W, L.nk, gs)
-    Wd = ogemv.dequant_dense(layer.canon)
+    layer, ref = make_layer(W, L.nk, gs)
+    Wd = ref.Wd
     rng = np.random.default_rng(5)
     cols = np.concatenate([[0, L.K - 1], rng.choice(L.K, 14, replace=False)])
     X = np.zeros((16, L.K), np.float16)
@@ -83,11 +79,10 @@ def test_configs_within_tolerance(L):
     W = L.W()
     gs = group_sizes(L, W)
     say(f"case config {L.name}")
-    layer = make_layer(W, L.nk, gs)
-    check_pack_matches_oracle(W, L.nk, gs, layer.canon)
+    layer, ref = make_layer(W, L.nk, gs)
     X = L.X(1)
     y = run_checked(layer, X)
-    y_ref, D, _ = oracle_y(layer.canon, X)
+    y_ref, D = ref.y(X)
     err = ogemv.normalized_error(y, y_ref, D)
     say(f"  {L.name}: normalised error {err:.3e}")
     assert err <= TOL
@@ -100,11 +95,11 @@ def test_beam_batches_within_tolerance(L):
     W = L.W()
     gs = group_sizes(L, W)
     say(f"case beam {L.name}")
-    layer = make_layer(W, L.nk, gs)
+    layer, ref = make_layer(W, L.nk, gs)
     for B in synth.CFG5_BATCHES:
         X = L.X(B)
         y = run_checked(layer, X)
-        y_ref, D, _ = oracle_y(layer.canon, X)
+        y_ref, D = ref.y(X)
         err = ogemv.normalized_error(y, y_ref, D)
         say(f"  B={B}: normalised error {err:.3e}")
         assert err <= TOL
@@ -113,16 +108,18 @@ def test_beam_batches_within_tolerance(L):
         assert ogemv.normalized_error(y1, y_ref[B - 1: B], D[B - 1: B]) <= TOL
 
 
-def test_decoder_set_sampled_layers_back_to_back():
-    """Layers 0 (2:4), 4 (1:4) and 31 (2:4) of the 32-layer set, all 7 projections, on one stream."""
-    Ls = [L for L in synth.cfg4() if L.layer in (0, 4, 31)]
+@pytest.mark.parametrize("layer_idx", [0, 4, 31])
+def test_decoder_layer_back_to_back(layer_idx):
+    """Decoder layers 0 (2:4), 4 (1:4) and 31 (2:4) of the 32-layer set: the 7
+    projections launched back to back on one stream, each with its own x."""
     import torch
+    Ls = [L for L in synth.cfg4() if L.layer == layer_idx]
     layers, xs, ys = [], [], []
     for L in Ls:
         W = L.W()
-        layers.append((L, make_layer(W, L.nk, group_sizes(L, W))))
-    say(f"case decoder set, {len(layers)} GEMVs back to back")
-    for L, layer in layers:
+        layers.append((L,) + make_layer(W, L.nk, group_sizes(L, W)))
+    say(f"case decoder layer {layer_idx}, {len(layers)} GEMVs back to back")
+    for L, layer, _ in layers:
         x = torch.from_numpy(L.X(1)).cuda()
         y = torch.empty((1, L.N), dtype=torch.float16, device="cuda")
         sg.run(layer.desc, layer.blob.data_ptr(), x.data_ptr(), y.data_ptr(), 1,
@@ -130,9 +127,8 @@ def test_decoder_set_sampled_layers_back_to_back():
         xs.append(x)
         ys.append(y)
     torch.cuda.synchronize()
-    for (L, layer), y in zip(layers, ys):
-        y_ref, D, _ = oracle_y(layer.canon, L.X(1))
-        err = ogemv.normalized_error(y.cpu().numpy(), y_ref, D)
+    for (L, layer, ref), y in zip(layers, ys):
+        err = ogemv.normalized_error(y.cpu().numpy(), *ref.y(L.X(1)))
         assert err <= TOL, (L.name, err)
 
 
@@ -143,18 +139,18 @@ def test_odd_shapes_and_batches(B):
         W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
         gs = rng.choice([32, 64, 128], N).astype(np.int32)
         say(f"case odd N={N} K={K} nk={nk} B={B}")
-        layer = make_layer(W, nk, gs)
+        layer, ref = make_layer(W, nk, gs)
         X = rng.standard_normal((B, K)).astype(np.float16)
         X[:, :8] = 0
         y = run_checked(layer, X)
-        y_ref, D, _ = oracle_y(layer.canon, X)
+        y_ref, D = ref.y(X)
         assert ogemv.normalized_error(y, y_ref, D) <= TOL
 
 
 def test_zero_input_gives_zero_output():
     rng = np.random.default_rng(9)
     W = (rng.standard_normal((64, 512)) * 0.02).astype(np.float16)
-    layer = make_layer(W, 2, np.full(64, 128, np.int32))
+    layer, _ = make_layer(W, 2, np.full(64, 128, np.int32))
     y = run_checked(layer, np.zeros((2, 512), np.float16))
     assert np.all(y.view(np.uint16) == 0)
 
@@ -167,14 +163,14 @@ def test_every_launch_geometry(nk, N, K):
     rng = np.random.default_rng(N + nk)
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
     gs = rng.choice([32, 64, 128, 256], N).astype(np.int32)
-    layer = make_layer(W, nk, gs)
+    layer, ref = make_layer(W, nk, gs)
     for B in (1, 2, 3, 4, 8, 16):
         pl = sg.plan(layer.desc, B)
         say(f"case geometry N={N} K={K} nk={nk} B={B} waves={pl.waves} cpw={pl.chunks_per_wave} "
             f"phase={pl.phase_chunks} xloads={pl.x_loads}")
         X = rng.standard_normal((B, K)).astype(np.float16)
         y = run_checked(layer, X)
-        y_ref, D, _ = oracle_y(layer.canon, X)
+        y_ref, D = ref.y(X)
         err = ogemv.normalized_error(y, y_ref, D)
         assert err <= TOL, (B, err)
 
@@ -196,8 +192,7 @@ def test_several_row_blocks_per_workgroup(nk, N, K):
     for g in np.unique(gs):
         rows = gs == g
         W[rows] = grid_weights(int(rows.sum()), K, nk, int(g), rng)
-    layer = make_layer(W, nk, gs)
-    Wd = ogemv.dequant_dense(layer.canon)
+    layer, ref = make_layer(W, nk, gs)
     for B in (4, 8, 9, 16):
         pl = sg.plan(layer.desc, B)
         want_rb = 4 if B >= 8 else 1
@@ -209,17 +204,13 @@ def test_several_row_blocks_per_workgroup(nk, N, K):
             idx = rng.choice(K, size=64, replace=False)
             X[b, idx] = rng.choice([-1.0, 1.0], 64)
         y = run_checked(layer, X)
-        y_ref = ogemv.gemv(Wd, X)
-        want = y_ref.astype(np.float16)
-        assert np.array_equal(want.astype(np.float64), y_ref), "reference not exact"
-        assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), f"B={B}"
+        assert_bit_exact(y, ref.y(X)[0], f"B={B}")
     # Gaussian weights and inputs: tolerance, then determinism
     Wg = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
-    layer = make_layer(Wg, nk, gs)
-    Wd = ogemv.dequant_dense(layer.canon)
+    layer, ref = make_layer(Wg, nk, gs)
     X = rng.standard_normal((16, K)).astype(np.float16)
     y = run_checked(layer, X)
-    err = ogemv.normalized_error(y, ogemv.gemv(Wd, X), ogemv.abs_dot(Wd, X))
+    err = ogemv.normalized_error(y, *ref.y(X))
     say(f"  gaussian B=16: normalised error {err:.3e}")
     assert err <= TOL
     y2 = run_checked(layer, X)
@@ -269,12 +260,9 @@ def test_group_launch_exact_arithmetic(nk):
                 idx = rng.choice(K, size=min(64, K), replace=False)
                 X[b, idx] = rng.choice([-1.0, 1.0], len(idx))
             Xs.append(X)
-        ys = _run_group_checked(layers, Xs, B)
-        for layer, X, y in zip(layers, Xs, ys):
-            y_ref, D, _ = oracle_y(layer.canon, X)
-            want = y_ref.astype(np.float16)
-            assert np.array_equal(want.astype(np.float64), y_ref), "reference not exact"
-            assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), (layer.desc.N, layer.desc.K, B)
+        ys = _run_group_checked([lay for lay, _ in layers], Xs, B)
+        for (layer, ref), X, y in zip(layers, Xs, ys):
+            assert_bit_exact(y, ref.y(X)[0], (layer.desc.N, layer.desc.K, B))
 
 
 def test_group_launch_many_small_layers():
@@ -288,24 +276,25 @@ def test_group_launch_many_small_layers():
         layers.append(make_layer(W, 2, gs))
         Xs.append(rng.standard_normal((2, K)).astype(np.float16))
     say("case group of 32 small layers")
-    ys = _run_group_checked(layers, Xs, 2)
-    for layer, X, y in zip(layers, Xs, ys):
-        y_ref, D, _ = oracle_y(layer.canon, X)
-        assert ogemv.normalized_error(y, y_ref, D) <= TOL
+    ys = _run_group_checked([lay for lay, _ in layers], Xs, 2)
+    for (layer, ref), X, y in zip(layers, Xs, ys):
+        assert ogemv.normalized_error(y, *ref.y(X)) <= TOL
 
 
 def test_group_launch_decoder_layer():
     """The GEMVs of decoder layer 0 grouped as a decode step issues them (q, k, v; o; gate, up; down)."""
     Ls = [L for L in synth.cfg4() if L.layer == 0]
-    made = {L.name: (L, make_layer(L.W(), L.nk, group_sizes(L, L.W()))) for L in Ls}
+    made = {}
+    for L in Ls:
+        W = L.W()
+        made[L.name] = (L,) + make_layer(W, L.nk, group_sizes(L, W))
     groups = [["q_proj", "k_proj", "v_proj"], ["o_proj"], ["gate_proj", "up_proj"], ["down_proj"]]
     for grp in groups:
         members = [made[f"cfg4_l00_{m}"] for m in grp]
         say(f"case group decoder layer 0: {grp}")
-        ys = _run_group_checked([lay for _, lay in members], [L.X(1) for L, _ in members], 1)
-        for (L, layer), y in zip(members, ys):
-            y_ref, D, _ = oracle_y(layer.canon, L.X(1))
-            err = ogemv.normalized_error(y, y_ref, D)
+        ys = _run_group_checked([lay for _, lay, _ in members], [L.X(1) for L, _, _ in members], 1)
+        for (L, layer, ref), y in zip(members, ys):
+            err = ogemv.normalized_error(y, *ref.y(L.X(1)))
             assert err <= TOL, (L.name, err)
             if len(grp) == 1:
                 # a group of one is the single call: same kernel, same geometry, same bits
@@ -316,19 +305,21 @@ def test_group_launch_decoder_layer():
 def test_activation_aware_pruned_layer(nk):
     """Weights pruned by |w| * ||x_k|| (sgemv_prune) through pack, layout and the
     kernel, against the oracle's scored selection quantised and multiplied in FP64."""
-    from oracle import prune as oprune, pack as opack
+    from oracle import prune as oprune, groups as ogroups
     L = synth.cfg2()[0]
     W = L.W()
     Xall = L.X(72)
     Xcal, X = Xall[:64], Xall[64:]
     Wp = sg.prune(W, nk, Xcal)
-    gs = sg.select_groups(Wp, nk, Xcal)
+    Wp_o = oprune.pruned_dense(W, oprune.nm_prune_scored(W, nk, Xcal)[1])
+    assert np.array_equal(Wp.view(np.uint16), Wp_o.view(np.uint16)), "sgemv_prune differs from the oracle"
+    _, mask = oprune.nm_prune(Wp_o, nk)
+    gs = ogroups.select_groups(Wp_o, mask, Xcal)
+    assert np.array_equal(sg.select_groups(Wp, nk, Xcal), gs)
     say(f"case activation-aware pruning nk={nk}")
-    layer = make_layer(Wp, nk, gs)
-    co = opack.pack_canonical(oprune.pruned_dense(W, oprune.nm_prune_scored(W, nk, Xcal)[1]), nk, gs)
-    Wd = ogemv.dequant_dense(co)
+    layer, ref = make_layer(Wp, nk, gs)
     y = run_checked(layer, X)
-    err = ogemv.normalized_error(y, ogemv.gemv(Wd, X), ogemv.abs_dot(Wd, X))
+    err = ogemv.normalized_error(y, *ref.y(X))
     say(f"  normalised error {err:.3e}")
     assert err <= TOL
 
@@ -342,12 +333,11 @@ def test_dense_ablation_within_tolerance(L):
     W = Ld.W()
     gs = group_sizes(Ld, W)
     say(f"case dense ablation {L.name}")
-    layer = make_layer(W, 4, gs)
-    check_pack_matches_oracle(W, 4, gs, layer.canon)
+    layer, ref = make_layer(W, 4, gs)
     for B in (1, 4):
         X = Ld.X(B)
         y = run_checked(layer, X)
-        y_ref, D, _ = oracle_y(layer.canon, X)
+        y_ref, D = ref.y(X)
         err = ogemv.normalized_error(y, y_ref, D)
         say(f"  B={B}: normalised error {err:.3e}")
         assert err <= TOL
@@ -361,7 +351,7 @@ def test_fp16_form_exact_arithmetic(nk, N, K):
     must equal the oracle's bits."""
     rng = np.random.default_rng(N + K + 7 * nk)
     W = (rng.integers(-8, 9, (N, K)) * 2.0 ** -6).astype(np.float16)
-    layer = sg.SparseGemvLayer.from_dense_fp16(W, nk)
+    layer, ref = make_layer_fp16(W, nk)
     say(f"case fp16 form exact nk={nk} N={N} K={K}")
     for B in (1, 3, 16):
         X = np.zeros((B, K), np.float16)
@@ -369,24 +359,18 @@ def test_fp16_form_exact_arithmetic(nk, N, K):
             idx = rng.choice(K, size=min(64, K), replace=False)
             X[b, idx] = rng.choice([-1.0, 1.0], len(idx))
         y = run_checked(layer, X)
-        y_ref, D, _ = oracle_y(layer.canon, X)
-        want = y_ref.astype(np.float16)
-        assert np.array_equal(want.astype(np.float64), y_ref), "reference not exact"
-        assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), B
+        assert_bit_exact(y, ref.y(X)[0], B)
 
 
 @pytest.mark.parametrize("L", synth.cfg3(), ids=lambda L: L.name + "_fp16")
 def test_fp16_form_mlp_within_tolerance(L):
-    from oracle import pack as opack
     W = L.W()
     say(f"case fp16 form {L.name}")
-    layer = sg.SparseGemvLayer.from_dense_fp16(W, L.nk)
-    co = opack.pack_fp16_canonical(W, L.nk)
-    assert np.array_equal(layer.canon["vals16"], co["vals16"])
+    layer, ref = make_layer_fp16(W, L.nk)
     for B in (1, 4):
         X = L.X(B)
         y = run_checked(layer, X)
-        y_ref, D, _ = oracle_y(layer.canon, X)
+        y_ref, D = ref.y(X)
         err = ogemv.normalized_error(y, y_ref, D)
         say(f"  B={B}: normalised error {err:.3e}")
         assert err <= TOL
@@ -397,13 +381,12 @@ def test_fp16_form_group_launch():
     layers, Xs = [], []
     for N, K in [(600, 4096), (33, 4096), (256, 1024)]:
         W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
-        layers.append(sg.SparseGemvLayer.from_dense_fp16(W, 2))
+        layers.append(make_layer_fp16(W, 2))
         Xs.append(rng.standard_normal((2, K)).astype(np.float16))
     say("case fp16 form group launch")
-    ys = _run_group_checked(layers, Xs, 2)
-    for layer, X, y in zip(layers, Xs, ys):
-        y_ref, D, _ = oracle_y(layer.canon, X)
-        assert ogemv.normalized_error(y, y_ref, D) <= TOL
+    ys = _run_group_checked([lay for lay, _ in layers], Xs, 2)
+    for (layer, ref), X, y in zip(layers, Xs, ys):
+        assert ogemv.normalized_error(y, *ref.y(X)) <= TOL
 
 
 @pytest.mark.parametrize("nk", [2, 1])
@@ -419,12 +402,19 @@ def test_large_layer_sampled_rows(nk):
     W = np.tile((rng.standard_normal((8192, K), dtype=np.float32) * 0.02).astype(np.float16), (N // 8192, 1))
     gs = np.full(N, 128, np.int32)
     say(f"case large layer nk={nk} N={N} K={K}")
-    layer = make_layer(W, nk, gs)
+    layer = sg.SparseGemvLayer.from_dense(W, nk, gs)
     say(f"  blob {layer.desc.blob_bytes / 2**20:.0f} MiB, grid {sg.plan(layer.desc, 1).grid}")
     X = rng.standard_normal((2, K)).astype(np.float16)
     y = run_checked(layer, X)
     rows = np.concatenate([[0, 1, N - 1, N - 16, N // 2], rng.choice(N, 59, replace=False)])
     co = opack.pack_canonical(W[rows], nk, gs[rows])
+    # the product's arrays for those rows equal the oracle's (uniform groups:
+    # row n's scale/zero words are n * K/128 ... (n + 1) * K/128 - 1)
+    for k in ("vals", "offs"):
+        assert np.array_equal(layer.canon[k][rows], co[k]), k
+    words = (rows[:, None] * (K // 128) + np.arange(K // 128)[None, :]).reshape(-1)
+    for k in ("scale", "zero"):
+        assert np.array_equal(layer.canon[k][words], co[k]), k
     Wd = ogemv.dequant_dense(co)
     y_ref, D = ogemv.gemv(Wd, X), ogemv.abs_dot(Wd, X)
     err = ogemv.normalized_error(y[:, rows], y_ref, D)
@@ -432,3 +422,145 @@ def test_large_layer_sampled_rows(nk):
     assert err <= TOL
     del layer
     torch.cuda.empty_cache()
+
+
+def degenerate_layer(N, K, rng):
+    """Gaussian rows (std 0.02) with hand-shaped degenerate rows on every
+    fifth row, cycling through: all +0; all -0; -0 among positive values;
+    every group one-signed positive; every group one-signed negative; values
+    x 1e-4 (FP16-subnormal values and scales); values x 3e-5 (scales that
+    round below 2^-24 and are raised to it); group 0 (columns 0 .. g - 1)
+    one-signed up to +65000; group 0 one-signed down to -65000. Group sizes
+    cycle through 32, 64, 128, 256 (rows of every kind at every size)."""
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    gs = np.array([32, 64, 128, 256], np.int32)[rng.integers(0, 4, N)]
+    special = np.arange(0, N, 5)
+    for i, n in enumerate(special):
+        kind = i % 9
+        g = int(gs[n])
+        row = rng.standard_normal(K) * 0.02
+        if kind == 0:
+            W[n] = np.float16(0.0)
+        elif kind == 1:
+            W[n] = np.float16(-0.0)
+        elif kind == 2:
+            r = np.abs(row).astype(np.float16)
+            r[rng.random(K) < 0.5] = np.float16(-0.0)
+            W[n] = r
+        elif kind == 3:
+            W[n] = np.abs(row).astype(np.float16)
+        elif kind == 4:
+            W[n] = (-np.abs(row)).astype(np.float16)
+        elif kind == 5:
+            W[n] = (row * 1e-4).astype(np.float16)
+        elif kind == 6:
+            W[n] = (row * 3e-5).astype(np.float16)
+        elif kind in (7, 8):
+            r = row.copy()
+            r[:g] = np.abs(r[:g]) / np.max(np.abs(r[:g])) * 65000.0
+            if kind == 8:
+                r[:g] = -r[:g]
+            W[n] = r.astype(np.float16)
+    return W, gs
+
+
+@pytest.mark.parametrize("nk", [2, 1, 4])
+def test_degenerate_groups_every_kernel(nk):
+    """Degenerate quantisation groups (all zero, -0, one-signed, FP16-subnormal
+    scales, values near 65000) through the one-vector, general, several-row-
+    block, dense and several-layer kernels. One-hot x: y equals the FP16
+    rounding of the oracle's column bit for bit (the kernel rounds each
+    dequantised weight once, as the cast of the exact value does). Gaussian
+    x, scaled by 2^-8 on the columns of the large groups so that y stays in
+    FP16 range: within the tolerance."""
+    rng = np.random.default_rng(500 + nk)
+    N, K = (10250, 2048) if nk != 4 else (1000, 2048)
+    W, gs = degenerate_layer(N, K, rng)
+    layer, ref = make_layer(W, nk, gs)
+    s = ref.co["scale"].view(np.float16).astype(np.float64)
+    assert np.any((s > 0) & (s < 2.0 ** -14)), "no FP16-subnormal scale in the layer"
+    assert np.max(np.abs(ref.Wd)) > 60000
+    cols = np.concatenate([[0, 1, 2, 3, 31, 32, 255, 256, K - 1], rng.choice(K, 7, replace=False)])
+    for B in (1, 3, 16):
+        pl = sg.plan(layer.desc, B)
+        say(f"case degenerate nk={nk} B={B} one-hot row_blocks={pl.row_blocks} waves={pl.waves}")
+        for c0 in range(0, len(cols), B):
+            cc = cols[c0: c0 + B]
+            X = np.zeros((len(cc), K), np.float16)
+            X[np.arange(len(cc)), cc] = 1.0
+            y = run_checked(layer, X)
+            want = ref.Wd[:, cc].T.astype(np.float16)
+            assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), (B, cc)
+    for B in (1, 3, 8, 16):
+        say(f"case degenerate nk={nk} B={B} gaussian")
+        X = rng.standard_normal((B, K))
+        X[:, :256] *= 2.0 ** -8
+        X = X.astype(np.float16)
+        y = run_checked(layer, X)
+        err = ogemv.normalized_error(y, *ref.y(X))
+        say(f"  normalised error {err:.3e}")
+        assert err <= TOL, (B, err)
+    # several layers in one launch: the degenerate layer beside a small one
+    Ws = (rng.standard_normal((40, 512)) * 0.02).astype(np.float16)
+    small, ref_s = make_layer(Ws, nk, np.full(40, 64, np.int32))
+    for B in (1, 3):
+        say(f"case degenerate nk={nk} B={B} group launch")
+        X = rng.standard_normal((B, K))
+        X[:, :256] *= 2.0 ** -8
+        X = X.astype(np.float16)
+        Xs = rng.standard_normal((B, 512)).astype(np.float16)
+        y, ys = _run_group_checked([layer, small], [X, Xs], B)
+        assert ogemv.normalized_error(y, *ref.y(X)) <= TOL
+        assert ogemv.normalized_error(ys, *ref_s.y(Xs)) <= TOL
+
+
+def test_stale_hip_error_is_not_reported_by_a_good_launch():
+    """A HIP error left on this thread by an earlier, unrelated runtime call
+    does not come back as SGEMV_EHIP from launches that succeed."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")      # the runtime this process already uses
+    rng = np.random.default_rng(31)
+    W = (rng.standard_normal((100, 1024)) * 0.02).astype(np.float16)
+    layer, ref = make_layer(W, 2, np.full(100, 128, np.int32))
+    X = rng.standard_normal((2, 1024)).astype(np.float16)
+    say("case stale HIP error before sgemv_run / sgemv_run_group / probes")
+    for B in (1, 2):
+        assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0      # leaves hipErrorInvalidDevice behind
+        y = run_checked(layer, X[:B])                            # raises SgemvError on a non-zero status
+        assert ogemv.normalized_error(y, *ref.y(X[:B])) <= TOL
+    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
+    (y,) = _run_group_checked([layer], [X], 2)
+    assert ogemv.normalized_error(y, *ref.y(X)) <= TOL
+    buf = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
+    dst = torch.zeros(64, dtype=torch.int32, device="cuda")
+    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
+    sg.probe_read(buf.data_ptr(), buf.numel(), dst.data_ptr(), 16, stream=torch.cuda.current_stream().cuda_stream)
+    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
+    sg.probe_empty(1, 64, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+
+
+def test_measurement_probes():
+    """The plain-read probe folds each lane's 16 bytes into one word (XOR of
+    its four words) and stores the words of the first store_bytes / 4 lanes;
+    the empty probe launches and returns."""
+    rng = np.random.default_rng(32)
+    nbytes = 3 * 4096 + 48                       # a last, partial workgroup
+    host = rng.integers(0, 2 ** 32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).cuda()
+    dst = torch.full((300,), -1, dtype=torch.int32, device="cuda")
+    say("case probes: read 12336 bytes, store 1024 bytes")
+    s = torch.cuda.current_stream().cuda_stream
+    magic = 0x9E3779B9                           # no lane's word equals it (checked below)
+    sg.probe_read(src.data_ptr(), nbytes, dst.data_ptr(), 1024, magic=magic, stream=s)
+    sg.probe_empty(4, 256, s)
+    torch.cuda.synchronize()
+    fold = np.bitwise_xor.reduce(host.reshape(-1, 4), axis=1)
+    assert not np.any(fold == magic)
+    got = dst.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got[:256], fold[:256])
+    assert np.all(got[256:] == 0xFFFFFFFF)     # only the 256 store lanes wrote
+    with pytest.raises(sg.SgemvError):
+        sg.probe_read(src.data_ptr(), nbytes + 8, dst.data_ptr(), 0, stream=s)
+    with pytest.raises(sg.SgemvError):
+        sg.probe_empty(1, 100, s)

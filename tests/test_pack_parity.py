@@ -58,12 +58,27 @@ def test_adaptive_mlp_configs(L):
     check_layer(L)
 
 
-def test_decoder_set_sampled_layers():
-    """32-layer set: every matrix shape at both N:M choices (layers 0 and 4), groups and blob."""
-    layers = [L for L in synth.cfg4() if L.layer in (0, 4) and L.name.split("_", 2)[2] in
-              ("q_proj", "gate_proj", "down_proj")]
-    for L in layers:
-        check_layer(L)
+def _check_decoder_matrix(i):
+    L = synth.cfg4()[i]
+    check_layer(L)
+    return L.name
+
+
+def test_decoder_set_every_matrix():
+    """All 224 matrices of the 32-layer set (which include the beam-batch
+    layers: their weights are those of decoder layers 0 and 4): group choice,
+    canonical arrays and blob bit-exact against the oracle. One matrix per
+    task, spread over worker processes (about 5 s of oracle work each)."""
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
+    n = len(synth.cfg4())
+    assert n == 224
+    assert {(L.K, L.N, L.nk, L.w_cfg, L.layer, L.mat) for L in synth.cfg5()} <= \
+        {(L.K, L.N, L.nk, L.w_cfg, L.layer, L.mat) for L in synth.cfg4()}
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("fork")) as ex:
+        done = list(ex.map(_check_decoder_matrix, range(n)))
+    assert done == [L.name for L in synth.cfg4()]
 
 
 @pytest.mark.parametrize("N,K,nk", [(200, 768, 2), (77, 1280, 1), (1, 256, 2), (15, 512, 1), (33, 11008, 2),
@@ -497,3 +512,14 @@ def test_layer_run_rejects_bad_buffers_before_any_launch():
     if torch.cuda.is_available():
         with pytest.raises(ValueError):
             layer.run(x.cuda())                                               # x on another device
+
+
+def test_select_groups_rejects_calibration_of_wrong_width():
+    """xcal must be [T, K]: a flat or narrower batch is refused before the
+    library reads T x K halves from it."""
+    W = np.zeros((8, 1024), np.float16)
+    with pytest.raises(ValueError):
+        sg.select_groups(W, 2, np.ones(4096, np.float16))
+    with pytest.raises(ValueError):
+        sg.select_groups(W, 2, np.ones((4, 512), np.float16))
+    assert sg.select_groups(W, 2, np.ones((4, 1024), np.float16)).shape == (8,)
