@@ -87,6 +87,7 @@ def parse():
     ap.add_argument("--no-small", action="store_true", help="skip the 1024x1024 and 4096x4096 layers")
     ap.add_argument("--no-hot", action="store_true", help="skip the cache-resident per-layer timing")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the empty-kernel and plain-read probes")
+    ap.add_argument("--no-list", action="store_true", help="skip the task-list launch figures")
     return ap.parse_args()
 
 
@@ -324,6 +325,41 @@ def main():
                                   "hot_us_per_call": None if us_hot is None else round(us_hot, 3),
                                   "grid": pl.grid, "waves": pl.waves, "chunks_per_wave": pl.chunks_per_wave}
 
+    # ---- the same four GEMVs as one task-list launch per step (cold copies
+    # cycled as in the step), and each layer alone as a task list
+    list_launch = None
+    if not args.no_list:
+        def body_list_steps(n=max(l["R"] for l in L_dev)):
+            cur = torch.cuda.current_stream(dev)
+            for i in range(n):
+                sg.run_list([(l["desc"], l["copies"][i % l["R"]].data_ptr(), l["x"].data_ptr(), l["y"].data_ptr())
+                             for l in L_dev], 1, cur.cuda_stream)
+
+        n_ls = max(l["R"] for l in L_dev)
+        us_ls = timed(body_list_steps, n_ls, 4, 1) * 1e3
+        pl = sg.plan_list([(l["desc"], 0, 0, 0) for l in L_dev], 1)
+        list_launch = {"us_per_step": round(us_ls, 3), "bytes": step_bytes,
+                       "GBps": round(step_bytes / (us_ls * 1e-6) / 1e9, 1),
+                       "pct_hbm_peak": round(100 * step_bytes / (us_ls * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+                       "grid": pl.grid, "waves": pl.waves, "layers_alone": {}}
+        for l in L_dev:
+            n_copies = l["R"]
+            n = n_copies * max(1, args.layer_calls // (n_copies * 4))
+
+            def body_list_one(l=l, n=n):
+                cur = torch.cuda.current_stream(dev)
+                for i in range(n):
+                    sg.run_list([(l["desc"], l["copies"][i % n_copies].data_ptr(), l["x"].data_ptr(),
+                                  l["y"].data_ptr())], 1, cur.cuda_stream)
+
+            us = timed(body_list_one, n, 4, 1) * 1e3
+            pl = sg.plan_list([(l["desc"], 0, 0, 0)], 1)
+            list_launch["layers_alone"][l["L"].name] = {
+                "us_per_call": round(us, 3), "GBps": round(l["bytes"] / (us * 1e-6) / 1e9, 1),
+                "pct_hbm_peak": round(100 * l["bytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+                "grid": pl.grid, "waves": pl.waves}
+        log("task-list launches timed")
+
     # ---- the practical ceiling of one launch, timed the same way: an empty
     # kernel, and a plain 16-byte-per-lane read of the layer's algorithmic
     # bytes less y (from the same cold copies), without and with a store of
@@ -543,13 +579,26 @@ def main():
             for tasks in grouped:
                 sg.run_group(tasks, 1, cur.cuda_stream)
 
+        # the task-list launch: 6 decoder layers (42 GEMVs) per launch, in
+        # layer order, 6 launches for the 32 layers
+        per_launch = 6 * len(names)
+        lists = [[(d, blob.data_ptr(), x.data_ptr(), y.data_ptr()) for (d, blob, x, y) in seq[i: i + per_launch]]
+                 for i in range(0, len(seq), per_launch)]
+
+        def body_list():
+            cur = torch.cuda.current_stream(dev)
+            for tasks in lists:
+                sg.run_list(tasks, 1, cur.cuda_stream)
+
         ms_seq = timed(body_decoder, 1, reps_dec, 2)
         ms_grp = timed(body_grouped, 1, reps_dec, 2)
+        ms_lst = timed(body_list, 1, reps_dec, 2)
         rate = lambda ms: {"us_per_sequence": round(ms * 1e3, 2), "GBps": round(dec_bytes / (ms * 1e-3) / 1e9, 1),
                            "pct_hbm_peak": round(100 * dec_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
         decoder = {"gemvs": len(seq), "bytes": dec_bytes, "replays": reps_dec,
                    "one_launch_per_gemv": dict(launches=len(seq), **rate(ms_seq)),
-                   "grouped_qkv_o_gateup_down": dict(launches=len(grouped), **rate(ms_grp))}
+                   "grouped_qkv_o_gateup_down": dict(launches=len(grouped), **rate(ms_grp)),
+                   "task_list": dict(launches=len(lists), gemvs_per_launch=per_launch, **rate(ms_lst))}
         del seq, packed
         torch.cuda.empty_cache()
         log("decoder sequence timed")
@@ -567,6 +616,7 @@ def main():
         "per_layer": per_layer,
         "roofline": roofline,
         "ceiling": ceiling,
+        "task_list": list_launch,
         "kernel_source_hash": khash,
         "pack_seconds": round(t_pack, 2),
     }

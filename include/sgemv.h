@@ -262,6 +262,40 @@ int sgemv_run_group(const sgemv_task* tasks, int32_t count, int32_t B, void* hip
  * Errors: as sgemv_run_group except EALIGN and EHIP. */
 int sgemv_plan_group(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_plan_t* out);
 
+#define SGEMV_LIST_MAX 48
+
+/* sgemv_run_list - up to SGEMV_LIST_MAX independent one-vector GEMVs
+ * y_i = W'_i x_i in one kernel launch, with no workspace: the task list
+ * travels in the kernel arguments. Per-token decoding runs every projection
+ * of every layer as a GEMV on one vector (P1 §1 "our core idea"); one launch
+ * per GEMV pays a kernel's dispatch, ramp-up and drain each time, which a
+ * few megabytes of weights cannot hide.
+ *   tasks      : host array of count layers in the INT4 form, each 2:4 or
+ *                1:4 (they may mix), any N and K (EINVAL for the FP16-valued
+ *                form or the dense ablation).
+ *   count      : 1..SGEMV_LIST_MAX.
+ *   B          : must be 1 (EINVAL otherwise).
+ *   hip_stream : hipStream_t to enqueue on (NULL = default stream).
+ * How the work is split: a workgroup of 8 waves (16 when some layer has
+ * more than 24 column chunks) computes a contiguous run of one layer's row
+ * blocks, prefetching each block's weights while computing the previous
+ * one; each layer gets workgroups in proportion to its algorithmic bytes,
+ * 256 of 16 waves or 512 of 8 in all (one or two per compute unit of
+ * MI355X), or fewer when the layers have fewer row blocks. The waves of a
+ * workgroup split each row's column chunks as sgemv_run does, so the
+ * results carry the bound of sgemv_run; the bits can differ from a separate
+ * call by FP32 reassociation. Outputs must not overlap each other, any x or
+ * any blob. Enqueues one kernel and returns without synchronising.
+ * Errors: EINVAL (count, B, NULL, value format), ESIZE (inconsistent
+ * descriptor), EALIGN, EHIP. */
+int sgemv_run_list(const sgemv_task* tasks, int32_t count, int32_t B, void* hip_stream);
+
+/* sgemv_plan_list - the launch sgemv_run_list would make (grid = the
+ * workgroups that have work; chunks_per_wave = the most any wave takes),
+ * without any HIP call. Device pointers are not examined.
+ * Errors: as sgemv_run_list except EALIGN and EHIP. */
+int sgemv_plan_list(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_plan_t* out);
+
 /* sgemv_strerror - static description of a status code (never NULL). */
 const char* sgemv_strerror(int code);
 

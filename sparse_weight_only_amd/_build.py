@@ -16,7 +16,7 @@ OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libsgemv.so")
 HOST_SRCS = ["host_pack.cpp", "host_layout.cpp"]
 HIP_SRCS = ["sgemv_k_nk1.hip", "sgemv_k_nk2.hip", "sgemv_k_nk4.hip", "sgemv_k_f16.hip", "sgemv_k_rb.hip", "sgemv_launch.hip",
-            "sgemv_probe.hip"]
+            "sgemv_probe.hip", "sgemv_k_list.hip"]
 
 
 def _hipcc() -> str:

@@ -1,6 +1,7 @@
 // sgemv_plan / sgemv_run: host-side checks and the launch of the SparseGemv kernel.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -8,12 +9,14 @@
 #include "internal.hpp"
 #include "kernels.hpp"
 #include "sgemv_device.hpp"
+#include "sgemv_list_device.hpp"
 
 using namespace sgemv;
 using sgemv_dev::GParams;
 using sgemv_dev::GroupFn;
 using sgemv_dev::kMaxGroup;
 static_assert(sgemv_dev::kMaxGroup == SGEMV_MAX_GROUP, "group size limit");
+static_assert(sgemv_dev::kListMax == SGEMV_LIST_MAX, "list size limit");
 using sgemv_dev::KernelFn;
 using sgemv_dev::KParams;
 
@@ -152,7 +155,146 @@ int make_group_plan(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_pla
   return SGEMV_OK;
 }
 
+// The task-list launch (one vector, INT4 form): the workgroups' count and
+// shape, and each task's share of them. Pure host arithmetic.
+//  - W = 16 waves per workgroup when the widest task has more than 24
+//    column chunks, else 8; each wave takes at most imax = ceil(C / W)
+//    chunks (rounded up to an instantiated size).
+//  - grid: at most 256 workgroups of 16 waves or 512 of 8 (one or two per
+//    compute unit of the 256 on MI355X, so that they are resident together),
+//    and no more than the row blocks of all tasks.
+//  - each task gets workgroups in proportion to its algorithmic bytes (at
+//    least one, at most its row blocks; largest remainders first), and its
+//    workgroup j computes a contiguous run of q + (j < r) row blocks. The
+//    launch grid is (largest share, tasks); workgroups past their task's
+//    share end at once.
+constexpr int kListCUs = 256;
+struct ListPlan { int waves, wlog, imax, grid, gx; int64_t lds; };
+int make_list_plan(const sgemv_task* tasks, int32_t count, int32_t B, ListPlan* lp, sgemv_dev::ListParams* g) {
+  if (!tasks || !lp) return SGEMV_EINVAL;
+  if (count < 1 || count > sgemv_dev::kListMax || B != 1) return SGEMV_EINVAL;
+  int cmax = 0;
+  int64_t blocks = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const sgemv_desc* d = tasks[i].desc;
+    if (!d) return SGEMV_EINVAL;
+    if (!desc_consistent(d)) return SGEMV_ESIZE;
+    if (d->value_format != 0 || (d->nk != 1 && d->nk != 2)) return SGEMV_EINVAL;
+    cmax = d->chunks > cmax ? d->chunks : cmax;
+    blocks += d->n_blocks;
+  }
+  ListPlan L;
+  L.waves = cmax > 24 ? 16 : 8;
+  L.wlog = L.waves == 16 ? 4 : 3;
+  const int need = (cmax + L.waves - 1) / L.waves;
+  L.imax = need <= 4 ? need : need <= 6 ? 6 : need <= 8 ? 8 : 0;
+  if (L.imax == 0) return SGEMV_ESIZE;
+  const int64_t cap = (int64_t)kListCUs * (L.waves == 16 ? 1 : 2);
+  L.grid = (int)(blocks < cap ? blocks : cap);
+  if (L.grid < count) L.grid = count;
+  L.lds = (int64_t)L.waves * L.imax * 512 + 2 * 256 * 4;
+  if (g) {
+    memset(g, 0, sizeof *g);
+    g->count = count;
+    g->wlog = L.wlog;
+    // workgroups per task in proportion to algorithmic bytes
+    double total = 0.0;
+    std::vector<double> cost(count);
+    for (int32_t i = 0; i < count; ++i) {
+      const sgemv_desc* d = tasks[i].desc;
+      cost[i] = (double)(d->vals_bytes + d->offs_bytes + 4 * d->n_groups + 2 * (int64_t)d->K + 2 * (int64_t)d->N);
+      total += cost[i];
+    }
+    std::vector<int> n(count);
+    std::vector<std::pair<double, int>> rem;
+    int used = 0;
+    for (int32_t i = 0; i < count; ++i) {
+      const double share = L.grid * cost[i] / total;
+      int k = (int)share;
+      if (k < 1) k = 1;
+      if (k > tasks[i].desc->n_blocks) k = tasks[i].desc->n_blocks;
+      n[i] = k;
+      used += k;
+      rem.emplace_back(share - k, i);
+    }
+    std::stable_sort(rem.begin(), rem.end(), [](const std::pair<double, int>& a, const std::pair<double, int>& b) {
+      return a.first > b.first;
+    });
+    for (size_t k = 0; used < L.grid && k < rem.size(); ++k) {
+      const int i = rem[k].second;
+      if (n[i] < tasks[i].desc->n_blocks) { ++n[i]; ++used; }
+    }
+    L.grid = used;
+    int nmax = 0;
+    for (int32_t i = 0; i < count; ++i) {
+      const sgemv_desc* d = tasks[i].desc;
+      sgemv_dev::ListTask& t = g->t[i];
+      t.blob = (const uint8_t*)tasks[i].blob_dev;
+      t.x = (const uint16_t*)tasks[i].x_dev;
+      t.y = (uint16_t*)tasks[i].y_dev;
+      t.blob_bytes = (uint32_t)d->blob_bytes;
+      t.off_offs = (uint32_t)d->off_offs;
+      t.off_perm = (uint32_t)d->off_perm;
+      t.off_sz = (uint32_t)d->off_sz;
+      t.N = d->N;
+      t.cls1 = d->class_rows[0];
+      t.cls2 = t.cls1 + d->class_rows[1];
+      t.cls3 = t.cls2 + d->class_rows[2];
+      t.c_nk = (uint32_t)d->chunks | ((uint32_t)d->nk << 16);
+      t.n_wg = n[i];
+      t.q = d->n_blocks / n[i];
+      t.r = d->n_blocks % n[i];
+      nmax = n[i] > nmax ? n[i] : nmax;
+    }
+    L.gx = nmax;
+  }
+  *lp = L;
+  return SGEMV_OK;
+}
+
 }  // namespace
+
+extern "C" int sgemv_plan_list(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_plan_t* out) {
+  if (!out) return SGEMV_EINVAL;
+  ListPlan L;
+  sgemv_dev::ListParams g;
+  const int rc = make_list_plan(tasks, count, B, &L, &g);
+  if (rc) return rc;
+  sgemv_plan_t q;
+  memset(&q, 0, sizeof q);
+  q.grid = L.grid;
+  q.row_blocks = 1;
+  q.lds_bytes = L.lds;
+  q.block = 64 * L.waves;
+  q.waves = L.waves;
+  q.chunks_per_wave = L.imax;
+  q.full_waves = L.waves;
+  q.phase_chunks = L.imax;
+  q.x_loads = (L.imax + 1) / 2;
+  *out = q;
+  return SGEMV_OK;
+}
+
+extern "C" int sgemv_run_list(const sgemv_task* tasks, int32_t count, int32_t B, void* hip_stream) {
+  ListPlan L;
+  sgemv_dev::ListParams g;
+  const int rc = make_list_plan(tasks, count, B, &L, &g);
+  if (rc) return rc;
+  for (int32_t i = 0; i < count; ++i) {
+    const sgemv_task& t = tasks[i];
+    if (!t.blob_dev || !t.x_dev || !t.y_dev) return SGEMV_EINVAL;
+    if (!aligned(t.blob_dev, t.x_dev, t.y_dev)) return SGEMV_EALIGN;
+  }
+  sgemv_dev::ListFn fn = sgemv_dev::get_list_kernel(L.imax);
+  if (!fn) return SGEMV_ESIZE;
+  (void)hipGetLastError();
+  if (ensure_lds((const void*)fn, L.lds)) return SGEMV_EHIP;
+  // grid (largest task share, tasks): workgroup (j, t) is task t's j-th
+  hipLaunchKernelGGL(fn, dim3((uint32_t)L.gx, (uint32_t)count), dim3(64 * L.waves), (uint32_t)L.lds,
+                     (hipStream_t)hip_stream, g);
+  if (hipGetLastError() != hipSuccess) return SGEMV_EHIP;
+  return SGEMV_OK;
+}
 
 extern "C" int sgemv_plan(const sgemv_desc* d, int32_t B, sgemv_plan_t* out) {
   return make_plan(d, B, out, nullptr);

@@ -97,6 +97,8 @@ def lib():
             "sgemv_plan": [D, i32, PL],
             "sgemv_run_group": [TK, i32, i32, P],
             "sgemv_plan_group": [TK, i32, i32, PL],
+            "sgemv_run_list": [TK, i32, i32, P],
+            "sgemv_plan_list": [TK, i32, i32, PL],
             "sgemv_probe_read": [P, i64, P, i64, u32, P],
             "sgemv_probe_empty": [i32, i32, P],
         }
@@ -289,6 +291,23 @@ def plan_group(tasks, B: int) -> Plan:
     """The launch sgemv_run_group would make; no GPU needed (pointers may be 0)."""
     pl = Plan()
     _check(lib().sgemv_plan_group(_tasks(tasks), len(tasks), B, ctypes.byref(pl)), "sgemv_plan_group")
+    return pl
+
+
+LIST_MAX = 48
+
+
+def run_list(tasks, B: int = 1, stream: int = 0) -> None:
+    """Enqueue up to LIST_MAX independent one-vector GEMVs (INT4 form, 2:4
+    and 1:4 may mix, any shapes) as one launch; ``tasks`` lists (desc,
+    blob_dev, x_dev, y_dev) with raw device pointers."""
+    _check(lib().sgemv_run_list(_tasks(tasks), len(tasks), B, ctypes.c_void_p(stream)), "sgemv_run_list")
+
+
+def plan_list(tasks, B: int = 1) -> Plan:
+    """The launch sgemv_run_list would make; no GPU needed (pointers may be 0)."""
+    pl = Plan()
+    _check(lib().sgemv_plan_list(_tasks(tasks), len(tasks), B, ctypes.byref(pl)), "sgemv_plan_list")
     return pl
 
 

@@ -516,28 +516,42 @@ def test_degenerate_groups_every_kernel(nk):
 
 def test_stale_hip_error_is_not_reported_by_a_good_launch():
     """A HIP error left on this thread by an earlier, unrelated runtime call
-    does not come back as SGEMV_EHIP from launches that succeed."""
+    does not come back as SGEMV_EHIP from launches that succeed (each entry
+    point is called right after the error is planted, with no other runtime
+    call in between)."""
     import ctypes
     hip = ctypes.CDLL("libamdhip64.so.7")      # the runtime this process already uses
     rng = np.random.default_rng(31)
     W = (rng.standard_normal((100, 1024)) * 0.02).astype(np.float16)
     layer, ref = make_layer(W, 2, np.full(100, 128, np.int32))
     X = rng.standard_normal((2, 1024)).astype(np.float16)
-    say("case stale HIP error before sgemv_run / sgemv_run_group / probes")
-    for B in (1, 2):
-        assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0      # leaves hipErrorInvalidDevice behind
-        y = run_checked(layer, X[:B])                            # raises SgemvError on a non-zero status
-        assert ogemv.normalized_error(y, *ref.y(X[:B])) <= TOL
-    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
-    (y,) = _run_group_checked([layer], [X], 2)
-    assert ogemv.normalized_error(y, *ref.y(X)) <= TOL
+    x = torch.from_numpy(X).cuda()
+    ys = [torch.zeros((2, 100), dtype=torch.float16, device="cuda") for _ in range(3)]
     buf = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda")
     dst = torch.zeros(64, dtype=torch.int32, device="cuda")
-    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
-    sg.probe_read(buf.data_ptr(), buf.numel(), dst.data_ptr(), 16, stream=torch.cuda.current_stream().cuda_stream)
-    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
-    sg.probe_empty(1, 64, torch.cuda.current_stream().cuda_stream)
+    s = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
+    say("case stale HIP error before sgemv_run / sgemv_run_group / probes")
+
+    def plant():
+        assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0     # leaves hipErrorInvalidDevice behind
+
+    plant()
+    sg.run(layer.desc, layer.blob.data_ptr(), x.data_ptr(), ys[0].data_ptr(), 1, s)   # raises on a non-zero status
+    plant()
+    sg.run(layer.desc, layer.blob.data_ptr(), x.data_ptr(), ys[1].data_ptr(), 2, s)
+    plant()
+    sg.run_group([(layer.desc, layer.blob.data_ptr(), x.data_ptr(), ys[2].data_ptr())], 2, s)
+    plant()
+    sg.probe_read(buf.data_ptr(), buf.numel(), dst.data_ptr(), 16, stream=s)
+    plant()
+    sg.probe_empty(1, 64, s)
+    assert hip.hipGetLastError() == 0          # each entry point cleared what it found
+    torch.cuda.synchronize()
+    y_ref, D = ref.y(X)
+    assert ogemv.normalized_error(ys[0].cpu().numpy()[:1], y_ref[:1], D[:1]) <= TOL
+    assert ogemv.normalized_error(ys[1].cpu().numpy(), y_ref, D) <= TOL
+    assert ogemv.normalized_error(ys[2].cpu().numpy(), y_ref, D) <= TOL
 
 
 def test_measurement_probes():
@@ -564,3 +578,110 @@ def test_measurement_probes():
         sg.probe_read(src.data_ptr(), nbytes + 8, dst.data_ptr(), 0, stream=s)
     with pytest.raises(sg.SgemvError):
         sg.probe_empty(1, 100, s)
+
+
+def _run_list_checked(layers, Xs, guard=64):
+    """One sgemv_run_list launch over one-vector layers (guarded outputs)."""
+    sentinel = np.uint16(0x7E5A)
+    bufs, tasks, xs = [], [], []
+    for layer, X in zip(layers, Xs):
+        N = layer.desc.N
+        x = torch.from_numpy(np.ascontiguousarray(X)).cuda()
+        ybuf = torch.full((N + 2 * guard,), int(np.int16(sentinel.view(np.int16))), dtype=torch.int16, device="cuda")
+        xs.append(x)
+        bufs.append(ybuf)
+        tasks.append((layer.desc, layer.blob.data_ptr(), x.data_ptr(), ybuf[guard:].data_ptr()))
+    sg.run_list(tasks, 1, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    out = []
+    for layer, ybuf in zip(layers, bufs):
+        host = ybuf.cpu().numpy().view(np.uint16)
+        assert np.all(host[:guard] == sentinel) and np.all(host[-guard:] == sentinel), "y guard band overwritten"
+        out.append(host[guard: guard + layer.desc.N].reshape(1, layer.desc.N).view(np.float16))
+    return out
+
+
+def test_list_launch_exact_arithmetic():
+    """Layers of different N, K and N:M in one task-list launch: bit-exact on
+    grid weights with x in {-1, 0, 1}; row-block runs of one to many blocks
+    per workgroup, layers of 1 to 43 column chunks, ragged last blocks."""
+    rng = np.random.default_rng(61)
+    specs = [(600, 4096, 2), (33, 4096, 1), (1000, 2048, 1), (77, 11008, 2), (16, 256, 2), (300, 4096, 1),
+             (4100, 1024, 2), (5, 768, 1), (2000, 11008, 1)]
+    layers, Xs = [], []
+    for N, K, nk in specs:
+        gs = rng.choice([32, 64, 128, 256], N).astype(np.int32)
+        W = np.zeros((N, K), np.float16)
+        for g in np.unique(gs):
+            W[gs == g] = grid_weights(int((gs == g).sum()), K, nk, int(g), rng)
+        layers.append(make_layer(W, nk, gs))
+        X = np.zeros((1, K), np.float16)
+        idx = rng.choice(K, size=min(64, K), replace=False)
+        X[0, idx] = rng.choice([-1.0, 1.0], len(idx))
+        Xs.append(X)
+    pl = sg.plan_list([(lay.desc, 0, 0, 0) for lay, _ in layers], 1)
+    say(f"case list exact, {len(specs)} layers: grid={pl.grid} waves={pl.waves} cpw={pl.chunks_per_wave}")
+    ys = _run_list_checked([lay for lay, _ in layers], Xs)
+    for (layer, ref), X, y in zip(layers, Xs, ys):
+        assert_bit_exact(y, ref.y(X)[0], (layer.desc.N, layer.desc.K, layer.desc.nk))
+    ys2 = _run_list_checked([lay for lay, _ in layers], Xs)
+    for y, y2 in zip(ys, ys2):
+        assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+
+
+def test_list_launch_mlp_layers_and_single_tasks():
+    """The four MLP layers (up/down at 1:4 and 2:4, adaptive groups) as one
+    list launch, and each alone (every workgroup then walks many blocks):
+    within the tolerance, the same bits on a second run."""
+    made = []
+    for L in synth.cfg3():
+        W = L.W()
+        made.append((L,) + make_layer(W, L.nk, group_sizes(L, W)))
+    say("case list: the four MLP layers in one launch")
+    ys = _run_list_checked([lay for _, lay, _ in made], [L.X(1) for L, _, _ in made])
+    for (L, layer, ref), y in zip(made, ys):
+        err = ogemv.normalized_error(y, *ref.y(L.X(1)))
+        say(f"  {L.name}: normalised error {err:.3e}")
+        assert err <= TOL, (L.name, err)
+    for L, layer, ref in made:
+        say(f"case list: {L.name} alone, grid {sg.plan_list([(layer.desc, 0, 0, 0)], 1).grid}")
+        (y,) = _run_list_checked([layer], [L.X(1)])
+        assert ogemv.normalized_error(y, *ref.y(L.X(1))) <= TOL
+        (y2,) = _run_list_checked([layer], [L.X(1)])
+        assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+
+
+def test_list_launch_decoder_layers():
+    """Decoder layers 3 (2:4) and 4 (1:4) of the 32-layer set: 14 GEMVs with
+    their own x in one launch, against the oracle."""
+    made = []
+    for L in synth.cfg4():
+        if L.layer in (3, 4):
+            W = L.W()
+            made.append((L,) + make_layer(W, L.nk, group_sizes(L, W)))
+    say(f"case list: decoder layers 3 and 4, {len(made)} GEMVs")
+    ys = _run_list_checked([lay for _, lay, _ in made], [L.X(1) for L, _, _ in made])
+    for (L, layer, ref), y in zip(made, ys):
+        err = ogemv.normalized_error(y, *ref.y(L.X(1)))
+        assert err <= TOL, (L.name, err)
+
+
+def test_list_launch_most_tasks():
+    """SGEMV_LIST_MAX (48) small layers in one launch, and the degenerate
+    groups layer among them."""
+    rng = np.random.default_rng(62)
+    layers, Xs = [], []
+    for i in range(sg.LIST_MAX - 1):
+        N, K = int(rng.integers(1, 90)), 256 * int(rng.integers(1, 12))
+        W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+        layers.append(make_layer(W, int(rng.choice([1, 2])), rng.choice([32, 64, 128, 256], N).astype(np.int32)))
+        Xs.append(rng.standard_normal((1, K)).astype(np.float16))
+    Wd, gs = degenerate_layer(3000, 2048, rng)
+    layers.append(make_layer(Wd, 1, gs))
+    X = rng.standard_normal((1, 2048))
+    X[:, :256] *= 2.0 ** -8
+    Xs.append(X.astype(np.float16))
+    say(f"case list: {len(layers)} layers")
+    ys = _run_list_checked([lay for lay, _ in layers], Xs)
+    for (layer, ref), X, y in zip(layers, Xs, ys):
+        assert ogemv.normalized_error(y, *ref.y(X)) <= TOL, (layer.desc.N, layer.desc.K)

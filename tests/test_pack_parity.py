@@ -523,3 +523,41 @@ def test_select_groups_rejects_calibration_of_wrong_width():
     with pytest.raises(ValueError):
         sg.select_groups(W, 2, np.ones((4, 512), np.float16))
     assert sg.select_groups(W, 2, np.ones((4, 1024), np.float16)).shape == (8,)
+
+
+def test_list_plan_and_host_errors():
+    """sgemv_plan_list / sgemv_run_list host checks and launch shape (no HIP
+    call before them)."""
+    E = sg.sgemv
+    rng = np.random.default_rng(12)
+    d_up = sg.describe(11008, 4096, 1, rng.choice([32, 128], 11008).astype(np.int32))
+    d_down = sg.describe(4096, 11008, 2, rng.choice([32, 128], 4096).astype(np.int32))
+    d_small = sg.describe(40, 1024, 2, np.full(40, 64, np.int32))
+    pl = sg.plan_list([(d_up, 0, 0, 0), (d_down, 0, 0, 0)], 1)
+    assert (pl.waves, pl.block, pl.chunks_per_wave, pl.grid) == (16, 1024, 3, 256)
+    pl = sg.plan_list([(d_up, 0, 0, 0)], 1)
+    assert (pl.waves, pl.chunks_per_wave, pl.grid) == (8, 2, 512)
+    pl = sg.plan_list([(d_small, 0, 0, 0)], 1)
+    assert pl.grid == 3                       # no more workgroups than row blocks
+    for tasks, B, code in [([], 1, E.SGEMV_EINVAL), ([(d_up, 0, 0, 0)], 2, E.SGEMV_EINVAL),
+                           ([(d_small, 0, 0, 0)] * 49, 1, E.SGEMV_EINVAL)]:
+        with pytest.raises(sg.SgemvError) as e:
+            sg.plan_list(tasks, B)
+        assert e.value.code == code
+    d16 = sg.describe_fp16(64, 1024, 2)
+    d4 = sg.describe(64, 1024, 4, np.full(64, 128, np.int32))
+    for d in (d16, d4):
+        with pytest.raises(sg.SgemvError) as e:
+            sg.plan_list([(d, 0, 0, 0)], 1)
+        assert e.value.code == E.SGEMV_EINVAL
+    bad = sg.describe(40, 1024, 2, np.full(40, 64, np.int32))
+    bad.n_blocks += 1
+    with pytest.raises(sg.SgemvError) as e:
+        sg.plan_list([(bad, 0, 0, 0)], 1)
+    assert e.value.code == E.SGEMV_ESIZE
+    # run: NULL and misaligned pointers are refused on the host
+    for ptrs, code in [((0, 0x1000, 0x1000), E.SGEMV_EINVAL), ((0x1001, 0x1000, 0x1000), E.SGEMV_EALIGN),
+                       ((0x1000, 0x1008, 0x1000), E.SGEMV_EALIGN)]:
+        with pytest.raises(sg.SgemvError) as e:
+            sg.run_list([(d_small,) + ptrs], 1, 0)
+        assert e.value.code == code
