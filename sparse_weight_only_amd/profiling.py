@@ -6,6 +6,8 @@ Usage (after the rocprofv3 runs named in each summary's header):
     python -m sparse_weight_only_amd.profiling traffic <fetch counter_collection.csv>
                      <write counter_collection.csv> <out.json> "<fetch command>" "<write command>"
     python -m sparse_weight_only_amd.profiling counters <out.txt> <counter_collection.csv>... -- "<command>"...
+    python -m sparse_weight_only_amd.profiling roofline <kernel_trace.csv> <bench.json> <out.txt>
+                     "<trace command>" "<bench command>"
 
 ``traffic`` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the
 same counters read for the 64 MiB reference copy that ``bench.py`` performs
@@ -71,6 +73,39 @@ def stats_summary(stats_csv: str, out_txt: str, command: str, trace_csv: str = N
             q = statistics.quantiles(v, n=10)
             lines.append(f"{name[:40]:40s} {grid:7d} {wg:5d} {len(v):6d} {statistics.mean(v):7.3f} "
                          f"{statistics.median(v):7.3f} {q[0]:7.3f} {q[-1]:7.3f}")
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def roofline_summary(trace_csv: str, bench_json: str, out_txt: str, command: str, bench_command: str) -> None:
+    """Per MLP layer: the traced dispatch duration (average and median over
+    the kernel trace), the HIP-event time per launch from a bench.py run
+    without the profiler, and the fraction of 8 TB/s that each implies for
+    the layer's algorithmic bytes."""
+    with open(bench_json) as f:
+        bench = json.loads(f.read().strip().splitlines()[-1])
+    by = defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]))
+        by[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"# roofline per MLP layer (kernel sources {kernel_source_hash()})",
+             f"# kernel trace: {command}",
+             f"# HIP events:   {bench_command}",
+             "# frac = algorithmic bytes / time / 8 TB/s",
+             "",
+             f"{'layer':30s} {'bytes':>9s} {'trace_avg':>9s} {'trace_med':>9s} {'event_us':>9s} "
+             f"{'frac_avg':>8s} {'frac_med':>8s} {'frac_evt':>8s}"]
+    for layer, (kname, grid) in _bench_layer_kernels().items():
+        pl = bench["per_layer"][layer]
+        v = [d for (n, gsz), ds in by.items() if kname in n and gsz == grid for d in ds]
+        if not v:
+            continue
+        avg, med, ev, nb = statistics.mean(v), statistics.median(v), pl["us_per_call"], pl["bytes"]
+        fr = lambda us: nb / (us * 1e-6) / 8e12
+        lines.append(f"{layer:30s} {nb:9d} {avg:9.3f} {med:9.3f} {ev:9.3f} {fr(avg):8.4f} {fr(med):8.4f} {fr(ev):8.4f}")
+    rf = bench.get("roofline", {})
+    lines += ["", f"bench.py roofline: kernel {rf.get('kernel')} frac {rf.get('frac')} "
+                  f"({rf.get('us_per_launch')} us per launch, {rf.get('timing')})"]
     with open(out_txt, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -160,6 +195,9 @@ def counters_summary(csvs, out_txt: str, commands, min_calls: int = 20) -> None:
 if __name__ == "__main__":
     if len(sys.argv) >= 5 and sys.argv[1] == "stats":
         stats_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5] if len(sys.argv) > 5 else None)
+    elif len(sys.argv) >= 7 and sys.argv[1] == "roofline":
+        # roofline <kernel_trace.csv> <bench.json> <out.txt> "<trace command>" "<bench command>"
+        roofline_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6])
     elif len(sys.argv) >= 4 and sys.argv[1] == "counters":
         # counters <out.txt> <csv>... -- <command>...
         sep = sys.argv.index("--")
