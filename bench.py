@@ -46,9 +46,10 @@ Beside the step, the same line reports
   4096 -> 4096, gate and up 4096 -> 11008, down 11008 -> 4096; 2:4 in the
   first and last 4 layers, 1:4 elsewhere), launched back to back on one
   stream, each with its own x and y; 20 replays of a graph of the whole
-  sequence, once with one launch per GEMV and once with the launches a
-  decode step can group (q, k and v together; o; gate and up together;
-  down: 4 launches per layer, sgemv_run_group). Every GEMV has its own device copy of its weights (1.79 GB in
+  sequence, once with one launch per GEMV, once with the launches a decode
+  step can group (q, k and v together; o; gate and up together; down: 4
+  launches per layer, sgemv_run_group), and once as task lists of 6 layers
+  (42 GEMVs) per launch (sgemv_run_list: 6 launches). Every GEMV has its own device copy of its weights (1.79 GB in
   all, so the sequence is cold by construction); the copies of one (shape,
   N:M) pair are filled from one packed matrix, since the kernel's work and
   bytes depend only on the shape, the N:M choice and the number of rows per
@@ -87,7 +88,6 @@ def parse():
     ap.add_argument("--no-small", action="store_true", help="skip the 1024x1024 and 4096x4096 layers")
     ap.add_argument("--no-hot", action="store_true", help="skip the cache-resident per-layer timing")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the empty-kernel and plain-read probes")
-    ap.add_argument("--no-list", action="store_true", help="skip the task-list launch figures")
     return ap.parse_args()
 
 
@@ -324,41 +324,6 @@ def main():
                                   "pct_hbm_peak": round(100 * l["bytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
                                   "hot_us_per_call": None if us_hot is None else round(us_hot, 3),
                                   "grid": pl.grid, "waves": pl.waves, "chunks_per_wave": pl.chunks_per_wave}
-
-    # ---- the same four GEMVs as one task-list launch per step (cold copies
-    # cycled as in the step), and each layer alone as a task list
-    list_launch = None
-    if not args.no_list:
-        def body_list_steps(n=max(l["R"] for l in L_dev)):
-            cur = torch.cuda.current_stream(dev)
-            for i in range(n):
-                sg.run_list([(l["desc"], l["copies"][i % l["R"]].data_ptr(), l["x"].data_ptr(), l["y"].data_ptr())
-                             for l in L_dev], 1, cur.cuda_stream)
-
-        n_ls = max(l["R"] for l in L_dev)
-        us_ls = timed(body_list_steps, n_ls, 4, 1) * 1e3
-        pl = sg.plan_list([(l["desc"], 0, 0, 0) for l in L_dev], 1)
-        list_launch = {"us_per_step": round(us_ls, 3), "bytes": step_bytes,
-                       "GBps": round(step_bytes / (us_ls * 1e-6) / 1e9, 1),
-                       "pct_hbm_peak": round(100 * step_bytes / (us_ls * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
-                       "grid": pl.grid, "waves": pl.waves, "layers_alone": {}}
-        for l in L_dev:
-            n_copies = l["R"]
-            n = n_copies * max(1, args.layer_calls // (n_copies * 4))
-
-            def body_list_one(l=l, n=n):
-                cur = torch.cuda.current_stream(dev)
-                for i in range(n):
-                    sg.run_list([(l["desc"], l["copies"][i % n_copies].data_ptr(), l["x"].data_ptr(),
-                                  l["y"].data_ptr())], 1, cur.cuda_stream)
-
-            us = timed(body_list_one, n, 4, 1) * 1e3
-            pl = sg.plan_list([(l["desc"], 0, 0, 0)], 1)
-            list_launch["layers_alone"][l["L"].name] = {
-                "us_per_call": round(us, 3), "GBps": round(l["bytes"] / (us * 1e-6) / 1e9, 1),
-                "pct_hbm_peak": round(100 * l["bytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
-                "grid": pl.grid, "waves": pl.waves}
-        log("task-list launches timed")
 
     # ---- the practical ceiling of one launch, timed the same way: an empty
     # kernel, and a plain 16-byte-per-lane read of the layer's algorithmic
@@ -616,7 +581,6 @@ def main():
         "per_layer": per_layer,
         "roofline": roofline,
         "ceiling": ceiling,
-        "task_list": list_launch,
         "kernel_source_hash": khash,
         "pack_seconds": round(t_pack, 2),
     }

@@ -276,23 +276,29 @@ int sgemv_plan_group(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_pl
  *   count      : 1..SGEMV_LIST_MAX.
  *   B          : must be 1 (EINVAL otherwise).
  *   hip_stream : hipStream_t to enqueue on (NULL = default stream).
- * How the work is split: a workgroup of 8 waves (16 when some layer has
- * more than 24 column chunks) computes a contiguous run of one layer's row
- * blocks, prefetching each block's weights while computing the previous
- * one; each layer gets workgroups in proportion to its algorithmic bytes,
- * 256 of 16 waves or 512 of 8 in all (one or two per compute unit of
- * MI355X), or fewer when the layers have fewer row blocks. The waves of a
- * workgroup split each row's column chunks as sgemv_run does, so the
- * results carry the bound of sgemv_run; the bits can differ from a separate
- * call by FP32 reassociation. Outputs must not overlap each other, any x or
- * any blob. Enqueues one kernel and returns without synchronising.
+ * How the work is split: each layer gets workgroups of 8 waves in
+ * proportion to its algorithmic bytes (up to 1536 in all, 6 per compute
+ * unit of MI355X); a workgroup stages its layer's x in LDS and its waves
+ * each walk a contiguous run of whole 16-row blocks, column chunk by column
+ * chunk, with the loads of the next chunks in flight. A row's sum runs over
+ * all its columns in one FP32 accumulator, so the results carry the bound
+ * of sgemv_run (with n the row's kept elements); the bits can differ from a
+ * separate sgemv_run by FP32 reassociation, and are the same on every call.
+ * It pays off when the layers together have many row blocks per wave (a
+ * decoder layer's 7 GEMVs, or more); a single layer is better served by
+ * sgemv_run, which splits each row over several waves.
+ * Outputs must not overlap each other, any x or any blob. Enqueues one
+ * kernel and returns without synchronising.
  * Errors: EINVAL (count, B, NULL, value format), ESIZE (inconsistent
- * descriptor), EALIGN, EHIP. */
+ * descriptor, or a layer whose share would exceed 256 row blocks a
+ * workgroup), EALIGN, EHIP. */
 int sgemv_run_list(const sgemv_task* tasks, int32_t count, int32_t B, void* hip_stream);
 
-/* sgemv_plan_list - the launch sgemv_run_list would make (grid = the
- * workgroups that have work; chunks_per_wave = the most any wave takes),
- * without any HIP call. Device pointers are not examined.
+/* sgemv_plan_list - the launch sgemv_run_list would make, without any HIP
+ * call: grid = workgroups with work, block = 64 * waves, row_blocks = the
+ * most row blocks a workgroup takes, lds_bytes = LDS per workgroup (the
+ * widest layer's x and a run's row indices and results). Device pointers
+ * are not examined.
  * Errors: as sgemv_run_list except EALIGN and EHIP. */
 int sgemv_plan_list(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_plan_t* out);
 

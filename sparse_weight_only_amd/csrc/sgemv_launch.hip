@@ -156,78 +156,79 @@ int make_group_plan(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_pla
 }
 
 // The task-list launch (one vector, INT4 form): the workgroups' count and
-// shape, and each task's share of them. Pure host arithmetic.
-//  - W = 16 waves per workgroup when the widest task has more than 24
-//    column chunks, else 8; each wave takes at most imax = ceil(C / W)
-//    chunks (rounded up to an instantiated size).
-//  - grid: at most 256 workgroups of 16 waves or 512 of 8 (one or two per
-//    compute unit of the 256 on MI355X, so that they are resident together),
-//    and no more than the row blocks of all tasks.
+// each task's share of them. Pure host arithmetic.
+//  - workgroups of 8 waves, at most 6 per compute unit of the 256 on MI355X
+//    (3 are resident at once with 72 VGPRs a lane; the others wait and take
+//    the place of those that finish first, which evens out the work of
+//    unequal runs), and each task's workgroups hold at least 8 of its row
+//    blocks where it has that many (one run per wave). Measured on the
+//    224-GEMV decoder as 6 launches: 2 per compute unit (all resident) took
+//    483 us with 8 chunks in flight a wave; 4 chunks with 4 and 6 per unit
+//    took 402-406 and 398-399 us, 8 per unit with 4 waves a workgroup 398 us;
 //  - each task gets workgroups in proportion to its algorithmic bytes (at
-//    least one, at most its row blocks; largest remainders first), and its
-//    workgroup j computes a contiguous run of q + (j < r) row blocks. The
-//    launch grid is (largest share, tasks); workgroups past their task's
-//    share end at once.
+//    least one, and enough that none takes more than 256 row blocks; largest
+//    remainders first), and its workgroup j computes a contiguous run of
+//    q + (j < r) row blocks, split over its waves. The launch grid is
+//    (largest share, tasks); workgroups past their task's share end at once.
 constexpr int kListCUs = 256;
-struct ListPlan { int waves, wlog, imax, grid, gx; int64_t lds; };
+constexpr int kListWgPerCU = 6;
+struct ListPlan { int waves, grid, gx, max_blocks; int64_t lds; };
 int make_list_plan(const sgemv_task* tasks, int32_t count, int32_t B, ListPlan* lp, sgemv_dev::ListParams* g) {
+  using sgemv_dev::kListMaxBlocks;
+  using sgemv_dev::kListWaves;
   if (!tasks || !lp) return SGEMV_EINVAL;
   if (count < 1 || count > sgemv_dev::kListMax || B != 1) return SGEMV_EINVAL;
   int cmax = 0;
-  int64_t blocks = 0;
+  double total = 0.0;
+  std::vector<double> cost(count);
+  std::vector<int> lo(count), hi(count);
+  int need = 0;
   for (int32_t i = 0; i < count; ++i) {
     const sgemv_desc* d = tasks[i].desc;
     if (!d) return SGEMV_EINVAL;
     if (!desc_consistent(d)) return SGEMV_ESIZE;
     if (d->value_format != 0 || (d->nk != 1 && d->nk != 2)) return SGEMV_EINVAL;
     cmax = d->chunks > cmax ? d->chunks : cmax;
-    blocks += d->n_blocks;
+    cost[i] = (double)(d->vals_bytes + d->offs_bytes + 4 * d->n_groups + 2 * (int64_t)d->K + 2 * (int64_t)d->N);
+    total += cost[i];
+    const int T = d->n_blocks;
+    lo[i] = (T + kListMaxBlocks - 1) / kListMaxBlocks;           // at most 256 blocks a workgroup
+    hi[i] = T / kListWaves > lo[i] ? T / kListWaves : lo[i];      // at least one block a wave, where possible
+    need += lo[i];
   }
   ListPlan L;
-  L.waves = cmax > 24 ? 16 : 8;
-  L.wlog = L.waves == 16 ? 4 : 3;
-  const int need = (cmax + L.waves - 1) / L.waves;
-  L.imax = need <= 4 ? need : need <= 6 ? 6 : need <= 8 ? 8 : 0;
-  if (L.imax == 0) return SGEMV_ESIZE;
-  const int64_t cap = (int64_t)kListCUs * (L.waves == 16 ? 1 : 2);
-  L.grid = (int)(blocks < cap ? blocks : cap);
-  if (L.grid < count) L.grid = count;
-  L.lds = (int64_t)L.waves * L.imax * 512 + 2 * 256 * 4;
-  if (g) {
-    memset(g, 0, sizeof *g);
-    g->count = count;
-    g->wlog = L.wlog;
-    // workgroups per task in proportion to algorithmic bytes
-    double total = 0.0;
-    std::vector<double> cost(count);
-    for (int32_t i = 0; i < count; ++i) {
-      const sgemv_desc* d = tasks[i].desc;
-      cost[i] = (double)(d->vals_bytes + d->offs_bytes + 4 * d->n_groups + 2 * (int64_t)d->K + 2 * (int64_t)d->N);
-      total += cost[i];
-    }
-    std::vector<int> n(count);
-    std::vector<std::pair<double, int>> rem;
-    int used = 0;
-    for (int32_t i = 0; i < count; ++i) {
-      const double share = L.grid * cost[i] / total;
-      int k = (int)share;
-      if (k < 1) k = 1;
-      if (k > tasks[i].desc->n_blocks) k = tasks[i].desc->n_blocks;
-      n[i] = k;
-      used += k;
-      rem.emplace_back(share - k, i);
-    }
-    std::stable_sort(rem.begin(), rem.end(), [](const std::pair<double, int>& a, const std::pair<double, int>& b) {
-      return a.first > b.first;
-    });
-    for (size_t k = 0; used < L.grid && k < rem.size(); ++k) {
-      const int i = rem[k].second;
-      if (n[i] < tasks[i].desc->n_blocks) { ++n[i]; ++used; }
-    }
-    L.grid = used;
-    int nmax = 0;
-    for (int32_t i = 0; i < count; ++i) {
-      const sgemv_desc* d = tasks[i].desc;
+  L.waves = kListWaves;
+  int grid = kListCUs * kListWgPerCU;
+  if (grid < need) grid = need;
+  std::vector<int> n(count);
+  std::vector<std::pair<double, int>> rem;
+  int used = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const double share = grid * cost[i] / total;
+    int k = (int)share;
+    k = k < lo[i] ? lo[i] : k > hi[i] ? hi[i] : k;
+    n[i] = k;
+    used += k;
+    rem.emplace_back(share - k, i);
+  }
+  std::stable_sort(rem.begin(), rem.end(), [](const std::pair<double, int>& a, const std::pair<double, int>& b) {
+    return a.first > b.first;
+  });
+  for (size_t k = 0; used < grid && k < rem.size(); ++k) {
+    const int i = rem[k].second;
+    if (n[i] < hi[i]) { ++n[i]; ++used; }
+  }
+  L.grid = used;
+  L.gx = 0;
+  L.max_blocks = 0;
+  if (g) memset(g, 0, sizeof *g);
+  for (int32_t i = 0; i < count; ++i) {
+    const sgemv_desc* d = tasks[i].desc;
+    const int q = d->n_blocks / n[i], r = d->n_blocks % n[i];
+    const int mb = q + (r ? 1 : 0);
+    L.max_blocks = mb > L.max_blocks ? mb : L.max_blocks;
+    L.gx = n[i] > L.gx ? n[i] : L.gx;
+    if (g) {
       sgemv_dev::ListTask& t = g->t[i];
       t.blob = (const uint8_t*)tasks[i].blob_dev;
       t.x = (const uint16_t*)tasks[i].x_dev;
@@ -242,12 +243,16 @@ int make_list_plan(const sgemv_task* tasks, int32_t count, int32_t B, ListPlan* 
       t.cls3 = t.cls2 + d->class_rows[2];
       t.c_nk = (uint32_t)d->chunks | ((uint32_t)d->nk << 16);
       t.n_wg = n[i];
-      t.q = d->n_blocks / n[i];
-      t.r = d->n_blocks % n[i];
-      nmax = n[i] > nmax ? n[i] : nmax;
+      t.q = q;
+      t.r = r;
     }
-    L.gx = nmax;
   }
+  if (g) g->count = count;
+  if (L.max_blocks > kListMaxBlocks) return SGEMV_ESIZE;
+  // x of the widest task, and the row indices and FP16 results of the most
+  // blocks a workgroup takes
+  L.lds = (int64_t)cmax * 512 + (int64_t)L.max_blocks * (64 + 32);
+  if (L.lds > 160 * 1024) return SGEMV_ESIZE;
   *lp = L;
   return SGEMV_OK;
 }
@@ -263,14 +268,14 @@ extern "C" int sgemv_plan_list(const sgemv_task* tasks, int32_t count, int32_t B
   sgemv_plan_t q;
   memset(&q, 0, sizeof q);
   q.grid = L.grid;
-  q.row_blocks = 1;
+  q.row_blocks = L.max_blocks;
   q.lds_bytes = L.lds;
   q.block = 64 * L.waves;
   q.waves = L.waves;
-  q.chunks_per_wave = L.imax;
+  q.chunks_per_wave = 0;
   q.full_waves = L.waves;
-  q.phase_chunks = L.imax;
-  q.x_loads = (L.imax + 1) / 2;
+  q.phase_chunks = 0;
+  q.x_loads = 0;
   *out = q;
   return SGEMV_OK;
 }
@@ -285,8 +290,7 @@ extern "C" int sgemv_run_list(const sgemv_task* tasks, int32_t count, int32_t B,
     if (!t.blob_dev || !t.x_dev || !t.y_dev) return SGEMV_EINVAL;
     if (!aligned(t.blob_dev, t.x_dev, t.y_dev)) return SGEMV_EALIGN;
   }
-  sgemv_dev::ListFn fn = sgemv_dev::get_list_kernel(L.imax);
-  if (!fn) return SGEMV_ESIZE;
+  sgemv_dev::ListFn fn = sgemv_dev::get_list_kernel();
   (void)hipGetLastError();
   if (ensure_lds((const void*)fn, L.lds)) return SGEMV_EHIP;
   // grid (largest task share, tasks): workgroup (j, t) is task t's j-th

@@ -533,12 +533,23 @@ def test_list_plan_and_host_errors():
     d_up = sg.describe(11008, 4096, 1, rng.choice([32, 128], 11008).astype(np.int32))
     d_down = sg.describe(4096, 11008, 2, rng.choice([32, 128], 4096).astype(np.int32))
     d_small = sg.describe(40, 1024, 2, np.full(40, 64, np.int32))
+    # 8 waves a workgroup, each with a run of at least one block where the
+    # task has that many: 688 and 256 blocks give at most 86 and 32 workgroups
     pl = sg.plan_list([(d_up, 0, 0, 0), (d_down, 0, 0, 0)], 1)
-    assert (pl.waves, pl.block, pl.chunks_per_wave, pl.grid) == (16, 1024, 3, 256)
+    assert (pl.waves, pl.block, pl.grid) == (8, 512, 86 + 32)
+    assert pl.lds_bytes == 43 * 512 + pl.row_blocks * 96      # x of K = 11008, rows and results of a run
     pl = sg.plan_list([(d_up, 0, 0, 0)], 1)
-    assert (pl.waves, pl.chunks_per_wave, pl.grid) == (8, 2, 512)
+    assert (pl.waves, pl.grid, pl.row_blocks) == (8, 86, 8)
     pl = sg.plan_list([(d_small, 0, 0, 0)], 1)
-    assert pl.grid == 3                       # no more workgroups than row blocks
+    assert pl.grid == 1 and pl.row_blocks == 3
+    # many tasks: at most 1536 workgroups (6 a compute unit), each with at
+    # least 8 blocks: 40 tasks of 256 blocks fill 40 x 32
+    many = [(sg.describe(4096, 4096, 1, np.full(4096, 128, np.int32)), 0, 0, 0) for i in range(40)]
+    pl = sg.plan_list(many, 1)
+    assert pl.grid == 1280 and pl.row_blocks == 8
+    big = [(sg.describe(4096 * 4, 4096, 1, np.full(4096 * 4, 128, np.int32)), 0, 0, 0) for i in range(40)]
+    pl = sg.plan_list(big, 1)
+    assert pl.grid == 1536 and pl.row_blocks <= 256
     for tasks, B, code in [([], 1, E.SGEMV_EINVAL), ([(d_up, 0, 0, 0)], 2, E.SGEMV_EINVAL),
                            ([(d_small, 0, 0, 0)] * 49, 1, E.SGEMV_EINVAL)]:
         with pytest.raises(sg.SgemvError) as e:
