@@ -685,3 +685,50 @@ def test_list_launch_most_tasks():
     ys = _run_list_checked([lay for lay, _ in layers], Xs)
     for (layer, ref), X, y in zip(layers, Xs, ys):
         assert ogemv.normalized_error(y, *ref.y(X)) <= TOL, (layer.desc.N, layer.desc.K)
+
+
+def _guarded(host_bytes, guard, fill):
+    """Device copy of host bytes between two sentinel bands (the copy stays 256-byte aligned)."""
+    buf = torch.full((host_bytes.size + 2 * guard,), fill, dtype=torch.uint8, device="cuda")
+    buf[guard: guard + host_bytes.size] = torch.from_numpy(np.ascontiguousarray(host_bytes)).cuda()
+    return buf
+
+
+def _bands_intact(buf, n, guard, fill):
+    h = buf.cpu().numpy()
+    return np.all(h[:guard] == fill) and np.all(h[guard + n:] == fill)
+
+
+@pytest.mark.parametrize("case", ["b1_2of4", "b1_1of4", "general_B3", "rows_B16", "dense_B1", "fp16_B2", "group_B1",
+                                  "list_B1"])
+def test_inputs_untouched_and_guard_bands(case):
+    """The kernels only read the blob and x: sentinel bands around both (and
+    the bytes themselves) are unchanged after a launch, and y is right."""
+    rng = np.random.default_rng(sum(map(ord, case)))
+    N, K, nk, B = {"b1_2of4": (300, 4096, 2, 1), "b1_1of4": (300, 11008, 1, 1), "general_B3": (200, 2048, 2, 3),
+                   "rows_B16": (10250, 2048, 1, 16), "dense_B1": (64, 1024, 4, 1), "fp16_B2": (100, 1024, 2, 2),
+                   "group_B1": (500, 4096, 1, 1), "list_B1": (700, 4096, 2, 1)}[case]
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    if case == "fp16_B2":
+        layer, ref = make_layer_fp16(W, nk)
+    else:
+        layer, ref = make_layer(W, nk, rng.choice([32, 128], N).astype(np.int32))
+    X = rng.standard_normal((B, K)).astype(np.float16)
+    G, FILL = 256, 0xA5
+    blob = _guarded(layer.blob_host, G, FILL)
+    xb = _guarded(X.view(np.uint8).reshape(-1), G, FILL)
+    y = torch.zeros((B, N), dtype=torch.float16, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    say(f"case guard bands {case}")
+    task = (layer.desc, blob[G:].data_ptr(), xb[G:].data_ptr(), y.data_ptr())
+    if case.startswith("group"):
+        sg.run_group([task], B, s)
+    elif case.startswith("list"):
+        sg.run_list([task], B, s)
+    else:
+        sg.run(layer.desc, blob[G:].data_ptr(), xb[G:].data_ptr(), y.data_ptr(), B, s)
+    torch.cuda.synchronize()
+    assert _bands_intact(blob, layer.blob_host.size, G, FILL) and _bands_intact(xb, X.nbytes, G, FILL)
+    assert np.array_equal(blob[G: G + layer.blob_host.size].cpu().numpy(), layer.blob_host)
+    assert np.array_equal(xb[G: G + X.nbytes].cpu().numpy().view(np.float16).reshape(B, K), X)
+    assert ogemv.normalized_error(y.cpu().numpy(), *ref.y(X)) <= TOL
