@@ -8,6 +8,13 @@ Usage (after the rocprofv3 runs named in each summary's header):
     python -m sparse_weight_only_amd.profiling counters <out.txt> <counter_collection.csv>... -- "<command>"...
     python -m sparse_weight_only_amd.profiling roofline <kernel_trace.csv> <bench.json> <out.txt>
                      "<trace command>" "<bench command>"
+    python -m sparse_weight_only_amd.profiling list <kernel_trace.csv> <fetch csv> <write csv> <sq csv>
+                     <out.txt> -- "<command>"...
+
+``list`` summarises the task-list launches of the decoder sequence: per
+launch position in the sequence, the traced duration, the algorithmic bytes
+(from the library's own descriptors of the decoder GEMVs), the scaled HBM
+bytes and the SQ counters.
 
 ``traffic`` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the
 same counters read for the 64 MiB reference copy that ``bench.py`` performs
@@ -192,6 +199,78 @@ def counters_summary(csvs, out_txt: str, commands, min_calls: int = 20) -> None:
         f.write("\n".join(lines) + "\n")
 
 
+def _decoder_list_bytes(per_launch_layers: int = 6):
+    """Algorithmic bytes of each task-list launch of the decoder sequence, in
+    launch order: the GEMVs of per_launch_layers consecutive decoder layers
+    per launch, each described by the library from its group selection."""
+    sys.path.insert(0, os.path.dirname(HERE))
+    import synth
+    import sparse_weight_only_amd as sg
+    descs = {}
+    for l in (0, 4):
+        for m, (name, K, N) in enumerate(synth.LLAMA7B_MATS):
+            key = (K, N, synth.layer_nk(l))
+            if key in descs:
+                continue
+            L = synth.Layer(f"decoder_l{l:02d}_{name}", K, N, key[2], True, 4, l, m, 4)
+            W = L.W()
+            gs = sg.select_groups(W, L.nk, L.Xcal(synth.CALIB_T), synth.FRAC_FINE, synth.G_FINE, synth.G_COARSE)
+            descs[key] = sg.describe(N, K, L.nk, gs)
+    seq = [sg.algorithmic_bytes(descs[(L.K, L.N, L.nk)], 1) for L in synth.cfg4()]
+    per = per_launch_layers * len(synth.LLAMA7B_MATS)
+    return [(len(seq[i:i + per]), sum(seq[i:i + per])) for i in range(0, len(seq), per)]
+
+
+def _list_rows(path: str, value_key: str, counter: str = None):
+    """The task-list kernel's dispatches of one run, in dispatch order."""
+    rows = [r for r in csv.DictReader(open(path)) if "sgemv_list_kernel" in r["Kernel_Name"]
+            and (counter is None or r["Counter_Name"] == counter)]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [float(r[value_key]) for r in rows]
+
+
+def list_summary(trace_csv: str, fetch_csv: str, write_csv: str, sq_csv: str, out_txt: str, commands) -> None:
+    launches = _decoder_list_bytes()
+    nl = len(launches)
+    dur = [(float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3
+           for r in sorted((r for r in csv.DictReader(open(trace_csv)) if "sgemv_list_kernel" in r["Kernel_Name"]),
+                           key=lambda r: int(r["Dispatch_Id"]))]
+    f_scale = REF_KIB / _reference(_counter_medians(fetch_csv, "FETCH_SIZE"))
+    w_scale = REF_KIB / _reference(_counter_medians(write_csv, "WRITE_SIZE"))
+    fetch = _list_rows(fetch_csv, "Counter_Value", "FETCH_SIZE")
+    write = _list_rows(write_csv, "Counter_Value", "WRITE_SIZE")
+    sq_names = sorted({r["Counter_Name"] for r in csv.DictReader(open(sq_csv))})
+    sq = {n: _list_rows(sq_csv, "Counter_Value", n) for n in sq_names}
+    for name, v in [("trace", dur), ("fetch", fetch), ("write", write)] + list(sq.items()):
+        if len(v) % nl:
+            raise RuntimeError(f"{name}: {len(v)} list dispatches is not a whole number of {nl}-launch passes")
+    pos = lambda v, i: v[i::nl]
+    med = statistics.median
+    lines = [f"# sgemv_list_kernel on the 224-GEMV decoder sequence, {nl} launches per pass "
+             f"(kernel sources {kernel_source_hash()})"]
+    lines += [f"# command: {c}" for c in commands]
+    lines += [f"# HBM bytes = FETCH_SIZE x {f_scale:.4f} + WRITE_SIZE x {w_scale:.4f} (KiB, scaled by the 64 MiB "
+              "reference copy of the same command); frac = algorithmic bytes / traced duration / 8 TB/s", ""]
+    lines.append(f"{'launch':>6s} {'gemvs':>5s} {'alg_bytes':>11s} {'calls':>5s} {'avg_us':>8s} {'med_us':>8s} "
+                 f"{'frac_med':>8s} {'hbm_bytes':>11s} {'hbm/alg':>7s}")
+    tot_alg = tot_us = 0.0
+    for i, (g, nb) in enumerate(launches):
+        d = pos(dur, i)
+        hbm = (med(pos(fetch, i)) * f_scale + med(pos(write, i)) * w_scale) * 1024
+        tot_alg += nb
+        tot_us += med(d)
+        lines.append(f"{i:6d} {g:5d} {nb:11d} {len(d):5d} {statistics.mean(d):8.2f} {med(d):8.2f} "
+                     f"{nb / (med(d) * 1e-6) / 8e12:8.4f} {int(hbm):11d} {hbm / nb:7.4f}")
+    lines.append(f"{'all':>6s} {sum(g for g, _ in launches):5d} {int(tot_alg):11d} {'':5s} {'':8s} {tot_us:8.2f} "
+                 f"{tot_alg / (tot_us * 1e-6) / 8e12:8.4f}")
+    lines += ["", "SQ counters per dispatch (median per launch position):",
+              f"{'launch':>6s} " + " ".join(f"{n:>16s}" for n in sq_names)]
+    for i in range(nl):
+        lines.append(f"{i:6d} " + " ".join(f"{med(pos(sq[n], i)):16.0f}" for n in sq_names))
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 5 and sys.argv[1] == "stats":
         stats_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5] if len(sys.argv) > 5 else None)
@@ -205,6 +284,10 @@ if __name__ == "__main__":
     elif len(sys.argv) >= 7 and sys.argv[1] == "traffic":
         print(json.dumps(traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6],
                                          _bench_layer_kernels()), indent=1))
+    elif len(sys.argv) >= 9 and sys.argv[1] == "list":
+        # list <trace.csv> <fetch.csv> <write.csv> <sq.csv> <out.txt> -- <command>...
+        sep = sys.argv.index("--")
+        list_summary(*sys.argv[2:7], sys.argv[sep + 1:])
     else:
         print(__doc__)
         sys.exit(2)
