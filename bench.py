@@ -372,6 +372,16 @@ def main():
     if ceiling is not None:
         c = ceiling["layers"][dom]
         roofline["frac_of_read_store_ceiling"] = round(c["read_store_us"] / d["us_per_call"], 4)
+    # bytes per dense weight and per kept element: algorithmic, and from the
+    # HBM counters where they were taken on these kernel sources
+    for l in L_dev:
+        L, pl = l["L"], per_layer[l["L"].name]
+        dense, kept = L.N * L.K, L.N * L.K * L.nk // 4
+        hbm = read_traffic(khash, L.name)
+        pl["alg_bytes_per_dense_weight"] = round(l["bytes"] / dense, 4)
+        pl["alg_bytes_per_kept"] = round(l["bytes"] / kept, 4)
+        pl["hbm_bytes_per_launch"] = hbm
+        pl["hbm_bytes_per_kept"] = None if hbm is None else round(hbm / kept, 4)
 
     def per_call_us(desc, copies, x, y, B, n_calls):
         n_copies = len(copies)
