@@ -48,8 +48,9 @@ Beside the step, the same line reports
   stream, each with its own x and y; 20 replays of a graph of the whole
   sequence, once with one launch per GEMV, once with the launches a decode
   step can group (q, k and v together; o; gate and up together; down: 4
-  launches per layer, sgemv_run_group), and once as task lists of 6 layers
-  (42 GEMVs) per launch (sgemv_run_list: 6 launches). Every GEMV has its own device copy of its weights (1.79 GB in
+  launches per layer, sgemv_run_group), and twice as task lists of 48 GEMVs
+  per launch (sgemv_run_list: 5 launches), once in the sequence order and
+  once grouped by (N:M, K, N). Every GEMV has its own device copy of its weights (1.79 GB in
   all, so the sequence is cold by construction); the copies of one (shape,
   N:M) pair are filled from one packed matrix, since the kernel's work and
   bytes depend only on the shape, the N:M choice and the number of rows per
@@ -554,26 +555,40 @@ def main():
             for tasks in grouped:
                 sg.run_group(tasks, 1, cur.cuda_stream)
 
-        # the task-list launch: 6 decoder layers (42 GEMVs) per launch, in
-        # layer order, 6 launches for the 32 layers
-        per_launch = 6 * len(names)
-        lists = [[(d, blob.data_ptr(), x.data_ptr(), y.data_ptr()) for (d, blob, x, y) in seq[i: i + per_launch]]
-                 for i in range(0, len(seq), per_launch)]
+        # task-list launches of 48 GEMVs (the kernel-argument limit), 5 for
+        # the 224: in the sequence order, and grouped by (N:M, K, N) so that a
+        # launch holds one or two shapes (the GEMVs are independent: each has
+        # its own x and y)
+        from sparse_weight_only_amd.profiling import LIST_PER_LAUNCH, decoder_list_order
+        keys = [(L.K, L.N, L.nk) for L in synth.cfg4()]
 
-        def body_list():
-            cur = torch.cuda.current_stream(dev)
-            for tasks in lists:
-                sg.run_list(tasks, 1, cur.cuda_stream)
+        def make_lists(by_shape):
+            order = [seq[i] for i in decoder_list_order(keys, by_shape)]
+            return [[(d, blob.data_ptr(), x.data_ptr(), y.data_ptr()) for (d, blob, x, y) in order[i: i + LIST_PER_LAUNCH]]
+                    for i in range(0, len(order), LIST_PER_LAUNCH)]
+
+        lists, lists_shape = make_lists(False), make_lists(True)
+
+        def body_lists(ls):
+            def body():
+                cur = torch.cuda.current_stream(dev)
+                for tasks in ls:
+                    sg.run_list(tasks, 1, cur.cuda_stream)
+            return body
 
         ms_seq = timed(body_decoder, 1, reps_dec, 2)
         ms_grp = timed(body_grouped, 1, reps_dec, 2)
-        ms_lst = timed(body_list, 1, reps_dec, 2)
+        ms_lst = timed(body_lists(lists), 1, reps_dec, 2)
+        ms_lsh = timed(body_lists(lists_shape), 1, reps_dec, 2)
         rate = lambda ms: {"us_per_sequence": round(ms * 1e3, 2), "GBps": round(dec_bytes / (ms * 1e-3) / 1e9, 1),
                            "pct_hbm_peak": round(100 * dec_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
         decoder = {"gemvs": len(seq), "bytes": dec_bytes, "replays": reps_dec,
                    "one_launch_per_gemv": dict(launches=len(seq), **rate(ms_seq)),
                    "grouped_qkv_o_gateup_down": dict(launches=len(grouped), **rate(ms_grp)),
-                   "task_list": dict(launches=len(lists), gemvs_per_launch=per_launch, **rate(ms_lst))}
+                   "task_list": dict(launches=len(lists), gemvs_per_launch=LIST_PER_LAUNCH, order="sequence",
+                                     **rate(ms_lst)),
+                   "task_list_by_shape": dict(launches=len(lists_shape), gemvs_per_launch=LIST_PER_LAUNCH,
+                                              order="grouped by N:M, K, N", **rate(ms_lsh))}
         del seq, packed
         torch.cuda.empty_cache()
         log("decoder sequence timed")

@@ -11,10 +11,10 @@ Usage (after the rocprofv3 runs named in each summary's header):
     python -m sparse_weight_only_amd.profiling list <kernel_trace.csv> <fetch csv> <write csv> <sq csv>
                      <out.txt> -- "<command>"...
 
-``list`` summarises the task-list launches of the decoder sequence: per
-launch position in the sequence, the traced duration, the algorithmic bytes
-(from the library's own descriptors of the decoder GEMVs), the scaled HBM
-bytes and the SQ counters.
+``list`` summarises the task-list launches of the decoder sequence (in the
+sequence order and grouped by shape): per launch position, the traced
+duration, the algorithmic bytes (from the library's own descriptors of the
+decoder GEMVs), the scaled HBM bytes and the SQ counters.
 
 ``traffic`` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the
 same counters read for the 64 MiB reference copy that ``bench.py`` performs
@@ -199,10 +199,23 @@ def counters_summary(csvs, out_txt: str, commands, min_calls: int = 20) -> None:
         f.write("\n".join(lines) + "\n")
 
 
-def _decoder_list_bytes(per_launch_layers: int = 6):
-    """Algorithmic bytes of each task-list launch of the decoder sequence, in
-    launch order: the GEMVs of per_launch_layers consecutive decoder layers
-    per launch, each described by the library from its group selection."""
+LIST_PER_LAUNCH = 48   # GEMVs per task-list launch of the decoder sequence (the kernel-argument limit)
+
+
+def decoder_list_order(keys, by_shape: bool):
+    """Order in which the task-list launches of the decoder sequence take its
+    GEMVs: the sequence order, or grouped by (N:M, K, N) (stable), so that
+    each launch holds GEMVs of one or two shapes. keys[i] = (K, N, nk) of
+    GEMV i. The launches take LIST_PER_LAUNCH GEMVs at a time in this order."""
+    idx = list(range(len(keys)))
+    if by_shape:
+        idx.sort(key=lambda i: (keys[i][2], keys[i][0], keys[i][1]))
+    return idx
+
+
+def _decoder_list_bytes(by_shape: bool):
+    """(GEMVs, algorithmic bytes) of each task-list launch of the decoder
+    sequence, each GEMV described by the library from its group selection."""
     sys.path.insert(0, os.path.dirname(HERE))
     import synth
     import sparse_weight_only_amd as sg
@@ -216,8 +229,10 @@ def _decoder_list_bytes(per_launch_layers: int = 6):
             W = L.W()
             gs = sg.select_groups(W, L.nk, L.Xcal(synth.CALIB_T), synth.FRAC_FINE, synth.G_FINE, synth.G_COARSE)
             descs[key] = sg.describe(N, K, L.nk, gs)
-    seq = [sg.algorithmic_bytes(descs[(L.K, L.N, L.nk)], 1) for L in synth.cfg4()]
-    per = per_launch_layers * len(synth.LLAMA7B_MATS)
+    keys = [(L.K, L.N, L.nk) for L in synth.cfg4()]
+    seq = [sg.algorithmic_bytes(descs[k], 1) for k in keys]
+    seq = [seq[i] for i in decoder_list_order(keys, by_shape)]
+    per = LIST_PER_LAUNCH
     return [(len(seq[i:i + per]), sum(seq[i:i + per])) for i in range(0, len(seq), per)]
 
 
@@ -230,8 +245,11 @@ def _list_rows(path: str, value_key: str, counter: str = None):
 
 
 def list_summary(trace_csv: str, fetch_csv: str, write_csv: str, sq_csv: str, out_txt: str, commands) -> None:
-    launches = _decoder_list_bytes()
-    nl = len(launches)
+    """Per launch position of the decoder sequence's task lists, for each of
+    the two orders bench.py times one after the other (the sequence order,
+    then grouped by shape; the same number of passes each): traced duration,
+    algorithmic bytes, counter-scaled HBM bytes and SQ counters."""
+    orders = [("sequence order", _decoder_list_bytes(False)), ("grouped by shape", _decoder_list_bytes(True))]
     dur = [(float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3
            for r in sorted((r for r in csv.DictReader(open(trace_csv)) if "sgemv_list_kernel" in r["Kernel_Name"]),
                            key=lambda r: int(r["Dispatch_Id"]))]
@@ -241,32 +259,39 @@ def list_summary(trace_csv: str, fetch_csv: str, write_csv: str, sq_csv: str, ou
     write = _list_rows(write_csv, "Counter_Value", "WRITE_SIZE")
     sq_names = sorted({r["Counter_Name"] for r in csv.DictReader(open(sq_csv))})
     sq = {n: _list_rows(sq_csv, "Counter_Value", n) for n in sq_names}
-    for name, v in [("trace", dur), ("fetch", fetch), ("write", write)] + list(sq.items()):
-        if len(v) % nl:
-            raise RuntimeError(f"{name}: {len(v)} list dispatches is not a whole number of {nl}-launch passes")
-    pos = lambda v, i: v[i::nl]
+    nl_all = sum(len(l) for _, l in orders)
     med = statistics.median
-    lines = [f"# sgemv_list_kernel on the 224-GEMV decoder sequence, {nl} launches per pass "
+    lines = [f"# sgemv_list_kernel on the 224-GEMV decoder sequence, {LIST_PER_LAUNCH} GEMVs a launch "
              f"(kernel sources {kernel_source_hash()})"]
     lines += [f"# command: {c}" for c in commands]
     lines += [f"# HBM bytes = FETCH_SIZE x {f_scale:.4f} + WRITE_SIZE x {w_scale:.4f} (KiB, scaled by the 64 MiB "
-              "reference copy of the same command); frac = algorithmic bytes / traced duration / 8 TB/s", ""]
-    lines.append(f"{'launch':>6s} {'gemvs':>5s} {'alg_bytes':>11s} {'calls':>5s} {'avg_us':>8s} {'med_us':>8s} "
-                 f"{'frac_med':>8s} {'hbm_bytes':>11s} {'hbm/alg':>7s}")
-    tot_alg = tot_us = 0.0
-    for i, (g, nb) in enumerate(launches):
-        d = pos(dur, i)
-        hbm = (med(pos(fetch, i)) * f_scale + med(pos(write, i)) * w_scale) * 1024
-        tot_alg += nb
-        tot_us += med(d)
-        lines.append(f"{i:6d} {g:5d} {nb:11d} {len(d):5d} {statistics.mean(d):8.2f} {med(d):8.2f} "
-                     f"{nb / (med(d) * 1e-6) / 8e12:8.4f} {int(hbm):11d} {hbm / nb:7.4f}")
-    lines.append(f"{'all':>6s} {sum(g for g, _ in launches):5d} {int(tot_alg):11d} {'':5s} {'':8s} {tot_us:8.2f} "
-                 f"{tot_alg / (tot_us * 1e-6) / 8e12:8.4f}")
-    lines += ["", "SQ counters per dispatch (median per launch position):",
-              f"{'launch':>6s} " + " ".join(f"{n:>16s}" for n in sq_names)]
-    for i in range(nl):
-        lines.append(f"{i:6d} " + " ".join(f"{med(pos(sq[n], i)):16.0f}" for n in sq_names))
+              "reference copy of the same command); frac = algorithmic bytes / traced duration / 8 TB/s"]
+    for name, v in [("trace", dur), ("fetch", fetch), ("write", write)] + list(sq.items()):
+        if len(v) % nl_all:
+            raise RuntimeError(f"{name}: {len(v)} list dispatches is not a whole number of passes of both orders")
+    first = 0
+    for title, launches in orders:
+        nl = len(launches)
+        part = lambda v: v[first * len(v) // nl_all: (first + nl) * len(v) // nl_all]
+        pos = lambda v, i: part(v)[i::nl]
+        lines += ["", f"{title}: {nl} launches a pass",
+                  f"{'launch':>6s} {'gemvs':>5s} {'alg_bytes':>11s} {'calls':>5s} {'avg_us':>8s} {'med_us':>8s} "
+                  f"{'frac_med':>8s} {'hbm_bytes':>11s} {'hbm/alg':>7s}"]
+        tot_alg = tot_us = 0.0
+        for i, (g, nb) in enumerate(launches):
+            d = pos(dur, i)
+            hbm = (med(pos(fetch, i)) * f_scale + med(pos(write, i)) * w_scale) * 1024
+            tot_alg += nb
+            tot_us += med(d)
+            lines.append(f"{i:6d} {g:5d} {nb:11d} {len(d):5d} {statistics.mean(d):8.2f} {med(d):8.2f} "
+                         f"{nb / (med(d) * 1e-6) / 8e12:8.4f} {int(hbm):11d} {hbm / nb:7.4f}")
+        lines.append(f"{'all':>6s} {sum(g for g, _ in launches):5d} {int(tot_alg):11d} {'':5s} {'':8s} {tot_us:8.2f} "
+                     f"{tot_alg / (tot_us * 1e-6) / 8e12:8.4f}")
+        lines += [f"SQ counters per dispatch (median per launch position):",
+                  f"{'launch':>6s} " + " ".join(f"{n:>16s}" for n in sq_names)]
+        for i in range(nl):
+            lines.append(f"{i:6d} " + " ".join(f"{med(pos(sq[n], i)):16.0f}" for n in sq_names))
+        first += nl
     with open(out_txt, "w") as f:
         f.write("\n".join(lines) + "\n")
 
