@@ -162,22 +162,30 @@ __device__ __forceinline__ void list_stream(const KParams& p, int B0, int nbw) {
   const auto rx = make_rsrc(p.x, (uint32_t)(C * 512));
 
   // 1. LDS: x (C * 512 bytes), then the original row indices of the
-  // workgroup's blocks (64 bytes a block), loaded by all lanes, then the
-  // blocks' FP16 results (32 bytes a block)
+  // workgroup's blocks (64 bytes a block), then the blocks' FP16 results (32
+  // bytes a block). x and the row indices go from memory straight to LDS
+  // (the buffer-to-LDS form of the load: lane l of a wave writes its 16
+  // bytes at the wave's LDS address + 16 l, no registers involved), and the
+  // waves issue the loads of their first chunks before the barrier waits for
+  // them, so that the staging and the first weights share one round trip.
+  typedef __attribute__((address_space(3))) void* LdsPtr;
   _Float16* xs = reinterpret_cast<_Float16*>(smem);
   int* ps = reinterpret_cast<int*>(smem + C * 512);
   uint16_t* ys = reinterpret_cast<uint16_t*>(ps + nbw * 16);
-  for (int u = tid; u < C * 32; u += 64 * W) reinterpret_cast<u32x4*>(xs)[u] = bload4<kCached>(rx, (uint32_t)u * 16u);
-  for (int u = tid; u < nbw * 4; u += 64 * W)
-    reinterpret_cast<u32x4*>(ps)[u] = bload4<kCached>(rbuf, p.off_perm + (uint32_t)(B0 * 64 + u * 16));
-  __syncthreads();
+  for (int u0 = 64 * w; u0 < C * 32; u0 += 64 * W)
+    if (u0 + lane < C * 32)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (LdsPtr)(smem + u0 * 16), 16, (uint32_t)(u0 + lane) * 16u, 0, 0,
+                                               kCached);
+  for (int u0 = 64 * w; u0 < nbw * 4; u0 += 64 * W)
+    if (u0 + lane < nbw * 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbuf, (LdsPtr)(smem + C * 512 + u0 * 16), 16,
+                                               p.off_perm + (uint32_t)(B0 * 64 + (u0 + lane) * 16), 0, 0, kCached);
 
   // 2. this wave's blocks: a contiguous run, nbw / W each, the first
   // nbw % W waves one more
   const int qq = nbw / W, rr = nbw % W;
   const int b0 = B0 + w * qq + (w < rr ? w : rr);
   const int nb = qq + (w < rr ? 1 : 0);
-  if (nb == 0) return;
   const int total = nb * C;
 
   const uint32_t lane_codes = (uint32_t)lane * (8u * NK), lane_offs = (uint32_t)lane * (4u * NK);
@@ -194,6 +202,8 @@ __device__ __forceinline__ void list_stream(const KParams& p, int B0, int nbw) {
     cursor_next(ic, p, r, q);
   }
   __builtin_amdgcn_s_setprio(0);
+  __syncthreads();
+  if (nb == 0) return;
 
   const uint32_t magic = opaque_vgpr(0x64006400u);
   const _Float16* xlane = xs + 64 * (q >> 1) + 8 * (q & 1);
