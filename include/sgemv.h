@@ -278,9 +278,12 @@ int sgemv_plan_group(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_pl
  *   hip_stream : hipStream_t to enqueue on (NULL = default stream).
  * How the work is split: each layer gets workgroups of 8 waves in
  * proportion to its algorithmic bytes (up to 1536 in all, 6 per compute
- * unit of MI355X); a workgroup stages its layer's x in LDS and its waves
- * each walk a contiguous run of whole 16-row blocks, column chunk by column
- * chunk, with the loads of the next chunks in flight. A row's sum runs over
+ * unit of MI355X), dispatched layer by layer in order of their longest
+ * wave's bytes, longest first (the order of the tasks does not matter); a
+ * workgroup stages its layer's x in LDS and its waves each walk a
+ * contiguous run of whole 16-row blocks, column chunk by column chunk, with
+ * the loads of the next chunks in flight. Launches whose layers share one
+ * shape balance best. A row's sum runs over
  * all its columns in one FP32 accumulator, so the results carry the bound
  * of sgemv_run (with n the row's kept elements); the bits can differ from a
  * separate sgemv_run by FP32 reassociation, and are the same on every call.
