@@ -604,10 +604,12 @@ def _run_list_checked(layers, Xs, guard=64):
 def test_list_launch_exact_arithmetic():
     """Layers of different N, K and N:M in one task-list launch: bit-exact on
     grid weights with x in {-1, 0, 1}; row-block runs of one to many blocks
-    per workgroup, layers of 1 to 43 column chunks, ragged last blocks."""
+    per workgroup, layers of 1 to 128 column chunks (K = 32768, the largest:
+    64 KiB of x in LDS), ragged last blocks. The same launch with the tasks
+    in reverse order gives the same bits per layer."""
     rng = np.random.default_rng(61)
     specs = [(600, 4096, 2), (33, 4096, 1), (1000, 2048, 1), (77, 11008, 2), (16, 256, 2), (300, 4096, 1),
-             (4100, 1024, 2), (5, 768, 1), (2000, 11008, 1)]
+             (4100, 1024, 2), (5, 768, 1), (2000, 11008, 1), (40, 32768, 2), (17, 32768, 1)]
     layers, Xs = [], []
     for N, K, nk in specs:
         gs = rng.choice([32, 64, 128, 256], N).astype(np.int32)
@@ -627,6 +629,9 @@ def test_list_launch_exact_arithmetic():
     ys2 = _run_list_checked([lay for lay, _ in layers], Xs)
     for y, y2 in zip(ys, ys2):
         assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+    ys3 = _run_list_checked([lay for lay, _ in layers][::-1], Xs[::-1])[::-1]
+    for y, y3 in zip(ys, ys3):
+        assert np.array_equal(y.view(np.uint16), y3.view(np.uint16))
 
 
 def test_list_launch_mlp_layers_and_single_tasks():
