@@ -27,7 +27,8 @@ Timing protocol
   copies and timed the same way as the layer;
 * the oracle (NumPy FP64 dequantise-then-dot, and the dot alone on the
   pre-decoded W') is timed on the host cores on passes over the same four
-  layers.
+  layers; for information, the library's packer and the oracle's pack the
+  four layers once each beside it.
 
 Beside the step, the same line reports
 * ``ablation``: the up and down MLP weights as a dense INT4 layer (every
@@ -133,19 +134,19 @@ def cpu_baseline(layers_host):
         blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in pools})) or "unknown"
     except Exception:
         threads, blas = int(os.environ.get("OMP_NUM_THREADS", "1")), "unknown"
-    total_bytes = sum(nb for (_, _, _, nb) in layers_host)
+    total_bytes = sum(l[3] for l in layers_host)
     t_dec = []
     passes = 3
     while len(t_dec) < passes:
         t0 = time.perf_counter()
-        for (name, canon, X, nbytes) in layers_host:
+        for (name, canon, X, nbytes, _, _) in layers_host:
             Wd = ogemv.dequant_dense(canon)
             ogemv.gemv(Wd, X)
             del Wd
         t_dec.append(time.perf_counter() - t0)
         if len(t_dec) == 1:
             passes = min(15, max(3, math.ceil(10.0 / t_dec[0])))
-    dense = [(ogemv.dequant_dense(canon), X) for (_, canon, X, _) in layers_host]
+    dense = [(ogemv.dequant_dense(canon), X) for (_, canon, X, _, _, _) in layers_host]
     t_dot = []
     for rep in range(6):
         t0 = time.perf_counter()
@@ -154,6 +155,20 @@ def cpu_baseline(layers_host):
         if rep:                                   # the first pass warms up
             t_dot.append(time.perf_counter() - t0)
     del dense
+    # information: the library's packer against the oracle's on the same
+    # weights and group sizes (prune, INT4 quantisation, 2bit-CSR arrays)
+    import sparse_weight_only_amd as sg
+    from oracle import pack as opack
+    t_lib = t_orc = 0.0
+    for (_, _, _, _, L, gs) in layers_host:
+        W = L.W()
+        t0 = time.perf_counter()
+        sg.pack(W, L.nk, gs)
+        t_lib += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        opack.pack_canonical(W, L.nk, gs)
+        t_orc += time.perf_counter() - t0
+        del W
     td, tt = statistics.median(t_dec), statistics.median(t_dot)
     return {"value": round(total_bytes / td / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "one pass over the 4 MLP layers: decode 2bit-CSR to dense FP64 W', then np.dot; "
@@ -161,6 +176,9 @@ def cpu_baseline(layers_host):
             "dot_only": {"value": round(total_bytes / tt / 1e9, 4), "unit": "GB/s",
                          "sample": f"np.dot on the pre-decoded FP64 W' of the 4 layers, median of 5 passes, "
                                    f"{tt * 1e3:.1f} ms per pass"},
+            "pack": {"library_s": round(t_lib, 3), "oracle_s": round(t_orc, 3),
+                     "sample": "the 4 MLP layers packed once each (prune, INT4 quantisation, 2bit-CSR arrays) "
+                               "from their FP16 weights and group sizes"},
             "affinity_cores": affinity, "blas": blas}
 
 
@@ -205,7 +223,7 @@ def main():
         L_dev.append({"L": L, "desc": desc, "blob_host": blob, "bytes": nbytes,
                       "x": torch.from_numpy(X).to(dev),
                       "y": torch.empty((1, L.N), dtype=torch.float16, device=dev)})
-        layers_host.append((L.name, canon, X, nbytes))
+        layers_host.append((L.name, canon, X, nbytes, L, gs))
     t_pack = time.perf_counter() - t_pack
     step_bytes = sum(l["bytes"] for l in L_dev)
     for l in L_dev:
