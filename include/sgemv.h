@@ -278,7 +278,8 @@ int sgemv_plan_group(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_pl
  *   hip_stream : hipStream_t to enqueue on (NULL = default stream).
  * How the work is split: each layer gets workgroups of 8 waves in
  * proportion to its algorithmic bytes (up to 1536 in all, 6 per compute
- * unit of MI355X), dispatched layer by layer in order of their longest
+ * unit of MI355X, or 3072 when the layers differ in shape or N:M choice),
+ * dispatched layer by layer in order of their longest
  * wave's bytes, longest first (the order of the tasks does not matter); a
  * workgroup stages its layer's x in LDS and its waves each walk a
  * contiguous run of whole 16-row blocks, column chunk by column chunk, with

@@ -158,6 +158,7 @@ int make_group_plan(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_pla
 // The task-list launch (one vector, INT4 form): the workgroups' count and
 // each task's share of them. Pure host arithmetic.
 //  - workgroups of 8 waves, at most 6 per compute unit of the 256 on MI355X
+//    (12 when the layers differ in shape or N:M choice, below)
 //    (3 are resident at once with 72 VGPRs a lane; the others wait and take
 //    the place of those that finish first, which evens out the work of
 //    unequal runs), and each task's workgroups hold at least 8 of its row
@@ -204,7 +205,17 @@ int make_list_plan(const sgemv_task* tasks, int32_t count, int32_t B, ListPlan* 
   }
   ListPlan L;
   L.waves = kListWaves;
-  int grid = kListCUs * kListWgPerCU;
+  // layers of different shapes or N:M choices: twice as many (smaller)
+  // workgroups, which even out the end of the launch where the layers'
+  // workgroups differ in length. Measured on the decoder sequence (three
+  // interleaved rounds): sequence order 360-363 us against 373-387 us,
+  // grouped by shape 338-340 us against 343-349 us; 12 per CU for every
+  // list made the lists of one shape slower.
+  bool mixed = false;
+  for (int32_t i = 1; i < count; ++i)
+    mixed |= tasks[i].desc->chunks != tasks[0].desc->chunks || tasks[i].desc->n_blocks != tasks[0].desc->n_blocks ||
+             tasks[i].desc->nk != tasks[0].desc->nk;
+  int grid = kListCUs * kListWgPerCU * (mixed ? 2 : 1);
   if (grid < need) grid = need;
   std::vector<int> n(count);
   std::vector<std::pair<double, int>> rem;
