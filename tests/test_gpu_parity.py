@@ -147,6 +147,28 @@ def test_odd_shapes_and_batches(B):
         assert ogemv.normalized_error(y, y_ref, D) <= TOL
 
 
+@pytest.mark.parametrize("nk", [2, 1])
+def test_every_batch_size(nk):
+    """Every batch size from 1 to 16 through the kernels the plan picks for it
+    (one vector, several vectors, 4 row blocks a workgroup from 8 vectors on
+    the 10250 x 2048 layer; phased x staging on the 11008-column one): within
+    the tolerance."""
+    rng = np.random.default_rng(700 + nk)
+    for (N, K) in [(10250, 2048), (300, 11008)]:
+        W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+        gs = rng.choice([32, 128], N).astype(np.int32)
+        layer, ref = make_layer(W, nk, gs)
+        X = rng.standard_normal((16, K)).astype(np.float16)
+        y_ref, D = ref.y(X)
+        for B in range(1, 17):
+            pl = sg.plan(layer.desc, B)
+            say(f"case batch N={N} K={K} nk={nk} B={B} row_blocks={pl.row_blocks} waves={pl.waves} "
+                f"phase={pl.phase_chunks}")
+            y = run_checked(layer, X[:B])
+            err = ogemv.normalized_error(y, y_ref[:B], D[:B])
+            assert err <= TOL, (N, K, B, err)
+
+
 def test_zero_input_gives_zero_output():
     rng = np.random.default_rng(9)
     W = (rng.standard_normal((64, 512)) * 0.02).astype(np.float16)
