@@ -282,6 +282,12 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
     }
     if constexpr (!V16) sv[i] = bload2<kStream>(rbuf, so, off);
     else sv[i] = u32x2{0u, 0u};
+    // with two chunks a wave, every wave's first chunk is requested before
+    // any second one, so that the last wave served has one chunk, not two,
+    // left to compute once its data is in. Measured: 0.07-0.1 us off each
+    // 4096 -> 11008 layer at one vector, neutral at 4 vectors; with four
+    // chunks a wave (12 waves) the same barrier made the call slower.
+    if (i == 0 && IMAX == 2) __builtin_amdgcn_s_barrier();
   }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (ONE) __builtin_amdgcn_s_setprio(0);
