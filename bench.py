@@ -51,7 +51,8 @@ Beside the step, the same line reports
   step can group (q, k and v together; o; gate and up together; down: 4
   launches per layer, sgemv_run_group), and twice as task lists of 48 GEMVs
   per launch (sgemv_run_list: 5 launches), once in the sequence order and
-  once grouped by (N:M, K, N). Every GEMV has its own device copy of its weights (1.79 GB in
+  once grouped by (N:M, K, N), and as one launch of all 224 from a task
+  table in device memory (sgemv_list_table + sgemv_run_list_table). Every GEMV has its own device copy of its weights (1.79 GB in
   all, so the sequence is cold by construction); the copies of one (shape,
   N:M) pair are filled from one packed matrix, since the kernel's work and
   bytes depend only on the shape, the N:M choice and the number of rows per
@@ -599,10 +600,19 @@ def main():
                     sg.run_list(tasks, 1, cur.cuda_stream)
             return body
 
+        # all 224 as one launch: the task table in device memory
+        table_host, table_launch = sg.list_table([(d, blob.data_ptr(), x.data_ptr(), y.data_ptr())
+                                                  for (d, blob, x, y) in seq], 1)
+        table_dev = torch.from_numpy(table_host).to(dev)
+
+        def body_table():
+            sg.run_list_table(table_dev.data_ptr(), table_launch, torch.cuda.current_stream(dev).cuda_stream)
+
         ms_seq = timed(body_decoder, 1, reps_dec, 2)
         ms_grp = timed(body_grouped, 1, reps_dec, 2)
         ms_lst = timed(body_lists(lists), 1, reps_dec, 2)
         ms_lsh = timed(body_lists(lists_shape), 1, reps_dec, 2)
+        ms_tab = timed(body_table, 1, reps_dec, 2)
         rate = lambda ms: {"us_per_sequence": round(ms * 1e3, 2), "GBps": round(dec_bytes / (ms * 1e-3) / 1e9, 1),
                            "pct_hbm_peak": round(100 * dec_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
         decoder = {"gemvs": len(seq), "bytes": dec_bytes, "replays": reps_dec,
@@ -611,8 +621,10 @@ def main():
                    "task_list": dict(launches=len(lists), gemvs_per_launch=LIST_PER_LAUNCH, order="sequence",
                                      **rate(ms_lst)),
                    "task_list_by_shape": dict(launches=len(lists_shape), gemvs_per_launch=LIST_PER_LAUNCH,
-                                              order="grouped by N:M, K, N", **rate(ms_lsh))}
-        del seq, packed
+                                              order="grouped by N:M, K, N", **rate(ms_lsh)),
+                   "task_table": dict(launches=1, gemvs_per_launch=len(seq), workgroups=table_launch.workgroups,
+                                      grid_rows=table_launch.rows, **rate(ms_tab))}
+        del seq, packed, table_dev
         torch.cuda.empty_cache()
         log("decoder sequence timed")
 

@@ -306,6 +306,55 @@ int sgemv_run_list(const sgemv_task* tasks, int32_t count, int32_t B, void* hip_
  * Errors: as sgemv_run_list except EALIGN and EHIP. */
 int sgemv_plan_list(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_plan_t* out);
 
+#define SGEMV_LIST_TABLE_MAX 4096
+
+/* The launch a task table describes (filled by sgemv_list_table). */
+typedef struct sgemv_list_launch {
+  int64_t table_bytes;     /* bytes of the table: rows * 80                          */
+  int64_t lds_bytes;       /* dynamic LDS per workgroup                              */
+  int64_t workgroups;      /* workgroups with work: the sum of the tasks' shares     */
+  int32_t rows;            /* grid rows, one table entry each                        */
+  int32_t row_width;       /* workgroups per grid row (at most 32)                   */
+  int32_t tasks;           /* count                                                  */
+  int32_t block;           /* lanes per workgroup (64 * 8)                           */
+} sgemv_list_launch;
+
+/* sgemv_list_table - the task list of sgemv_run_list for any number of
+ * one-vector GEMVs (a whole decoder step: P1 §1 "our core idea" runs every
+ * projection of every layer per token), planned once on the host into a
+ * table that the caller keeps in device memory, so that one launch covers
+ * them all and the per-launch ramp-up and drain are paid once.
+ *   tasks       : host array of count layers, as for sgemv_run_list.
+ *   count       : 1..SGEMV_LIST_TABLE_MAX.
+ *   B           : must be 1 (EINVAL otherwise).
+ *   table_host  : host buffer for the table, or NULL to fill *out only.
+ *   table_bytes : its size; ESIZE if below out->table_bytes.
+ *   out         : host pointer, the launch (grid, LDS, table size).
+ * The split is that of sgemv_run_list, with 1536 (3072 for mixed shapes)
+ * workgroups per 48 tasks or part of them, so each task gets the share it
+ * would get in a list of 48. The table holds the tasks' device pointers and
+ * their share: build it again when any of them changes. Pure host work, no
+ * HIP call.
+ * Errors: EINVAL (count, B, NULL, value format), ESIZE (inconsistent
+ * descriptor, a share over 256 row blocks a workgroup, table too small),
+ * EALIGN (a blob, x or y pointer). */
+int sgemv_list_table(const sgemv_task* tasks, int32_t count, int32_t B, void* table_host,
+                     int64_t table_bytes, sgemv_list_launch* out);
+
+/* sgemv_run_list_table - enqueue the launch of a task table.
+ *   table_dev  : device copy of the bytes sgemv_list_table wrote, 16-byte
+ *                aligned; it must hold launch->rows entries, stay unchanged
+ *                and stay allocated until the kernel has run.
+ *   launch     : host pointer to the launch sgemv_list_table filled for it.
+ *   hip_stream : hipStream_t to enqueue on (NULL = default stream).
+ * Results are bit-for-bit those of sgemv_run_list on the same tasks (a
+ * row's sum does not depend on which workgroup computes it), and the same
+ * on every call. Outputs must not overlap each other, any x or any blob.
+ * Enqueues one kernel and returns without synchronising.
+ * Errors: EINVAL (NULL, a launch field out of range), EALIGN (table_dev),
+ * EHIP. */
+int sgemv_run_list_table(const void* table_dev, const sgemv_list_launch* launch, void* hip_stream);
+
 /* sgemv_strerror - static description of a status code (never NULL). */
 const char* sgemv_strerror(int code);
 

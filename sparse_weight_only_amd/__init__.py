@@ -9,5 +9,5 @@ from .sgemv import (  # noqa: F401
     SgemvError, Desc, Plan, lib, lib_path, describe, select_groups, prune, pack, layout, run, plan, strerror,
     SparseGemvLayer, algorithmic_bytes, Task, MAX_GROUP, run_group, plan_group,
     describe_fp16, pack_fp16, layout_fp16, f64_to_f16, probe_read, probe_empty,
-    LIST_MAX, run_list, plan_list,
+    LIST_MAX, run_list, plan_list, LIST_TABLE_MAX, ListLaunch, list_table, run_list_table,
 )

@@ -177,14 +177,19 @@ int make_group_plan(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_pla
 //    units of 8 blocks, so that a workgroup's waves get the same number of
 //    blocks, was slower (386-395 us): the workgroups of a layer then differ
 //    by a whole unit.
+//  - a table launch (the task table in device memory, any number of tasks)
+//    has kListWgPerCU x 256 workgroups (doubled for mixed shapes) per
+//    kListMax tasks or part of it, so that each task gets the share it
+//    would get in a launch of kListMax tasks.
 constexpr int kListCUs = 256;
 constexpr int kListWgPerCU = 6;
 struct ListPlan { int waves, grid, gx, max_blocks; int64_t lds; };
-int make_list_plan(const sgemv_task* tasks, int32_t count, int32_t B, ListPlan* lp, sgemv_dev::ListParams* g) {
+int make_list_plan(const sgemv_task* tasks, int32_t count, int32_t B, int32_t max_count, ListPlan* lp,
+                   std::vector<sgemv_dev::ListTask>* out) {
   using sgemv_dev::kListMaxBlocks;
   using sgemv_dev::kListWaves;
   if (!tasks || !lp) return SGEMV_EINVAL;
-  if (count < 1 || count > sgemv_dev::kListMax || B != 1) return SGEMV_EINVAL;
+  if (count < 1 || count > max_count || B != 1) return SGEMV_EINVAL;
   int cmax = 0;
   double total = 0.0;
   std::vector<double> cost(count);
@@ -215,7 +220,7 @@ int make_list_plan(const sgemv_task* tasks, int32_t count, int32_t B, ListPlan* 
   for (int32_t i = 1; i < count; ++i)
     mixed |= tasks[i].desc->chunks != tasks[0].desc->chunks || tasks[i].desc->n_blocks != tasks[0].desc->n_blocks ||
              tasks[i].desc->nk != tasks[0].desc->nk;
-  int grid = kListCUs * kListWgPerCU * (mixed ? 2 : 1);
+  int grid = kListCUs * kListWgPerCU * (mixed ? 2 : 1) * ((count + sgemv_dev::kListMax - 1) / sgemv_dev::kListMax);
   if (grid < need) grid = need;
   std::vector<int> n(count);
   std::vector<std::pair<double, int>> rem;
@@ -238,7 +243,7 @@ int make_list_plan(const sgemv_task* tasks, int32_t count, int32_t B, ListPlan* 
   L.grid = used;
   L.gx = 0;
   L.max_blocks = 0;
-  if (g) memset(g, 0, sizeof *g);
+  if (out) out->assign(count, sgemv_dev::ListTask{});
   // grid rows in order of the longest wave's bytes, longest first: the
   // workgroups are dispatched row after row, so the long ones start first
   // and the short ones fill the end of the launch
@@ -256,8 +261,8 @@ int make_list_plan(const sgemv_task* tasks, int32_t count, int32_t B, ListPlan* 
     const int mb = q + (r ? 1 : 0);
     L.max_blocks = mb > L.max_blocks ? mb : L.max_blocks;
     L.gx = n[i] > L.gx ? n[i] : L.gx;
-    if (g) {
-      sgemv_dev::ListTask& t = g->t[k];
+    if (out) {
+      sgemv_dev::ListTask& t = (*out)[k];
       t.blob = (const uint8_t*)tasks[i].blob_dev;
       t.x = (const uint16_t*)tasks[i].x_dev;
       t.y = (uint16_t*)tasks[i].y_dev;
@@ -275,7 +280,6 @@ int make_list_plan(const sgemv_task* tasks, int32_t count, int32_t B, ListPlan* 
       t.r = r;
     }
   }
-  if (g) g->count = count;
   if (L.max_blocks > kListMaxBlocks) return SGEMV_ESIZE;
   // x of the widest task, and the row indices and FP16 results of the most
   // blocks a workgroup takes
@@ -285,13 +289,25 @@ int make_list_plan(const sgemv_task* tasks, int32_t count, int32_t B, ListPlan* 
   return SGEMV_OK;
 }
 
+// Grid rows of a table launch: a task whose share is wider than a row spans
+// consecutive rows (workgroups past the share in its last row end at once).
+constexpr int kListRowWidth = 32;
+
+bool list_pointers_ok(const sgemv_task* tasks, int32_t count, int* rc) {
+  for (int32_t i = 0; i < count; ++i) {
+    const sgemv_task& t = tasks[i];
+    if (!t.blob_dev || !t.x_dev || !t.y_dev) { *rc = SGEMV_EINVAL; return false; }
+    if (!aligned(t.blob_dev, t.x_dev, t.y_dev)) { *rc = SGEMV_EALIGN; return false; }
+  }
+  return true;
+}
+
 }  // namespace
 
 extern "C" int sgemv_plan_list(const sgemv_task* tasks, int32_t count, int32_t B, sgemv_plan_t* out) {
   if (!out) return SGEMV_EINVAL;
   ListPlan L;
-  sgemv_dev::ListParams g;
-  const int rc = make_list_plan(tasks, count, B, &L, &g);
+  const int rc = make_list_plan(tasks, count, B, sgemv_dev::kListMax, &L, nullptr);
   if (rc) return rc;
   sgemv_plan_t q;
   memset(&q, 0, sizeof q);
@@ -310,20 +326,72 @@ extern "C" int sgemv_plan_list(const sgemv_task* tasks, int32_t count, int32_t B
 
 extern "C" int sgemv_run_list(const sgemv_task* tasks, int32_t count, int32_t B, void* hip_stream) {
   ListPlan L;
-  sgemv_dev::ListParams g;
-  const int rc = make_list_plan(tasks, count, B, &L, &g);
+  std::vector<sgemv_dev::ListTask> order;
+  int rc = make_list_plan(tasks, count, B, sgemv_dev::kListMax, &L, &order);
   if (rc) return rc;
-  for (int32_t i = 0; i < count; ++i) {
-    const sgemv_task& t = tasks[i];
-    if (!t.blob_dev || !t.x_dev || !t.y_dev) return SGEMV_EINVAL;
-    if (!aligned(t.blob_dev, t.x_dev, t.y_dev)) return SGEMV_EALIGN;
-  }
+  if (!list_pointers_ok(tasks, count, &rc)) return rc;
+  sgemv_dev::ListParams g;
+  memset(&g, 0, sizeof g);
+  g.count = count;
+  std::copy(order.begin(), order.end(), g.t);
   sgemv_dev::ListFn fn = sgemv_dev::get_list_kernel();
   (void)hipGetLastError();
   if (ensure_lds((const void*)fn, L.lds)) return SGEMV_EHIP;
   // grid (largest task share, tasks): workgroup (j, t) is task t's j-th
   hipLaunchKernelGGL(fn, dim3((uint32_t)L.gx, (uint32_t)count), dim3(64 * L.waves), (uint32_t)L.lds,
                      (hipStream_t)hip_stream, g);
+  if (hipGetLastError() != hipSuccess) return SGEMV_EHIP;
+  return SGEMV_OK;
+}
+
+extern "C" int sgemv_list_table(const sgemv_task* tasks, int32_t count, int32_t B, void* table_host,
+                                int64_t table_bytes, sgemv_list_launch* out) {
+  if (!out) return SGEMV_EINVAL;
+  ListPlan L;
+  std::vector<sgemv_dev::ListTask> order;
+  int rc = make_list_plan(tasks, count, B, SGEMV_LIST_TABLE_MAX, &L, &order);
+  if (rc) return rc;
+  if (!list_pointers_ok(tasks, count, &rc)) return rc;
+  const int width = L.gx < kListRowWidth ? L.gx : kListRowWidth;
+  std::vector<sgemv_dev::ListRow> rows;
+  for (const sgemv_dev::ListTask& t : order)
+    for (int j0 = 0; j0 < t.n_wg; j0 += width) {
+      sgemv_dev::ListRow row;
+      memset(&row, 0, sizeof row);
+      row.t = t;
+      row.j0 = j0;
+      rows.push_back(row);
+    }
+  if (rows.size() > 65535) return SGEMV_ESIZE;   // grid rows
+  sgemv_list_launch q;
+  memset(&q, 0, sizeof q);
+  q.table_bytes = (int64_t)(rows.size() * sizeof(sgemv_dev::ListRow));
+  q.lds_bytes = L.lds;
+  q.workgroups = L.grid;
+  q.rows = (int32_t)rows.size();
+  q.row_width = width;
+  q.tasks = count;
+  q.block = 64 * L.waves;
+  *out = q;
+  if (!table_host) return SGEMV_OK;
+  if (table_bytes < q.table_bytes) return SGEMV_ESIZE;
+  memcpy(table_host, rows.data(), (size_t)q.table_bytes);
+  return SGEMV_OK;
+}
+
+extern "C" int sgemv_run_list_table(const void* table_dev, const sgemv_list_launch* launch, void* hip_stream) {
+  if (!table_dev || !launch) return SGEMV_EINVAL;
+  const sgemv_list_launch& q = *launch;
+  if (q.rows < 1 || q.rows > 65535 || q.row_width < 1 || q.row_width > kListRowWidth ||
+      q.block != 64 * sgemv_dev::kListWaves || q.lds_bytes < 0 || q.lds_bytes > 160 * 1024 ||
+      q.table_bytes != (int64_t)q.rows * (int64_t)sizeof(sgemv_dev::ListRow))
+    return SGEMV_EINVAL;
+  if ((uintptr_t)table_dev % 16) return SGEMV_EALIGN;
+  sgemv_dev::ListTableFn fn = sgemv_dev::get_list_table_kernel();
+  (void)hipGetLastError();
+  if (ensure_lds((const void*)fn, q.lds_bytes)) return SGEMV_EHIP;
+  hipLaunchKernelGGL(fn, dim3((uint32_t)q.row_width, (uint32_t)q.rows), dim3((uint32_t)q.block), (uint32_t)q.lds_bytes,
+                     (hipStream_t)hip_stream, (const sgemv_dev::ListRow*)table_dev);
   if (hipGetLastError() != hipSuccess) return SGEMV_EHIP;
   return SGEMV_OK;
 }

@@ -28,7 +28,7 @@
 
 namespace sgemv_dev {
 
-// One task of a list launch (76 bytes; up to kListMax of them travel in the
+// One task of a list launch (72 bytes; up to kListMax of them travel in the
 // kernel arguments, which are limited to 4 KiB).
 struct ListTask {
   const uint8_t* blob;     // kernel-layout blob
@@ -49,7 +49,19 @@ struct ListParams {
   int32_t pad[3];
   ListTask t[kListMax];
 };
+static_assert(sizeof(ListTask) == 72, "task layout");
 static_assert(sizeof(ListParams) <= 4096, "kernel arguments are limited to 4 KiB");
+
+// One grid row of a table launch (the task table sits in device memory, so
+// a launch can hold any number of tasks): workgroup (i, row) is workgroup
+// j0 + i of the row's task. A task whose share is wider than a row spans
+// consecutive rows.
+struct ListRow {
+  ListTask t;
+  int32_t j0;
+  int32_t pad;
+};
+static_assert(sizeof(ListRow) == 80, "table row layout");
 
 // The loads of one chunk of one wave: codes, offsets and scale|zero words.
 template <int NK>
@@ -247,12 +259,10 @@ __device__ __forceinline__ void list_stream(const KParams& p, int B0, int nbw) {
   }
 }
 
-// Workgroup (j, t) of the grid (max_t n_wg, count): workgroup j of task t,
-// which takes row blocks [j q + min(j, r), ... + q + (j < r)); workgroups
-// with j >= n_wg of their task have no work and end at once.
-__device__ __forceinline__ void list_block(const ListParams& g) {
-  const int t = (int)blockIdx.y, j = (int)blockIdx.x;
-  const ListTask& T = g.t[t];
+// Workgroup j of task T, which takes row blocks [j q + min(j, r), ... + q +
+// (j < r)); workgroups with j >= n_wg of their task have no work and end at
+// once.
+__device__ __forceinline__ void list_task(const ListTask& T, const int j) {
   if (j >= T.n_wg) return;
   const int B0 = j * T.q + (j < T.r ? j : T.r);
   const int nbw = T.q + (j < T.r ? 1 : 0);
@@ -278,7 +288,15 @@ __device__ __forceinline__ void list_block(const ListParams& g) {
   else list_stream<1>(p, B0, nbw);
 }
 
+// Workgroup (j, t) of the grid (max_t n_wg, count) of a kernel-argument
+// launch: workgroup j of task t.
+__device__ __forceinline__ void list_block(const ListParams& g) {
+  list_task(g.t[blockIdx.y], (int)blockIdx.x);
+}
+
 typedef void (*ListFn)(ListParams);
 ListFn get_list_kernel();
+typedef void (*ListTableFn)(const ListRow*);
+ListTableFn get_list_table_kernel();
 
 }  // namespace sgemv_dev

@@ -236,9 +236,12 @@ def _decoder_list_bytes(by_shape: bool):
     return [(len(seq[i:i + per]), sum(seq[i:i + per])) for i in range(0, len(seq), per)]
 
 
-def _list_rows(path: str, value_key: str, counter: str = None):
-    """The task-list kernel's dispatches of one run, in dispatch order."""
-    rows = [r for r in csv.DictReader(open(path)) if "sgemv_list_kernel" in r["Kernel_Name"]
+LIST_KERNEL, TABLE_KERNEL = "sgemv_list_kernel", "sgemv_list_table_kernel"
+
+
+def _list_rows(path: str, value_key: str, counter: str = None, kernel: str = LIST_KERNEL):
+    """The dispatches of one task-list kernel in one run, in dispatch order."""
+    rows = [r for r in csv.DictReader(open(path)) if kernel in r["Kernel_Name"]
             and (counter is None or r["Counter_Name"] == counter)]
     rows.sort(key=lambda r: int(r["Dispatch_Id"]))
     return [float(r[value_key]) for r in rows]
@@ -247,12 +250,14 @@ def _list_rows(path: str, value_key: str, counter: str = None):
 def list_summary(trace_csv: str, fetch_csv: str, write_csv: str, sq_csv: str, out_txt: str, commands) -> None:
     """Per launch position of the decoder sequence's task lists, for each of
     the two orders bench.py times one after the other (the sequence order,
-    then grouped by shape; the same number of passes each): traced duration,
-    algorithmic bytes, counter-scaled HBM bytes and SQ counters."""
+    then grouped by shape; the same number of passes each), and for the one
+    table launch of all 224 GEMVs: traced duration, algorithmic bytes,
+    counter-scaled HBM bytes and SQ counters."""
     orders = [("sequence order", _decoder_list_bytes(False)), ("grouped by shape", _decoder_list_bytes(True))]
-    dur = [(float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3
-           for r in sorted((r for r in csv.DictReader(open(trace_csv)) if "sgemv_list_kernel" in r["Kernel_Name"]),
-                           key=lambda r: int(r["Dispatch_Id"]))]
+    durations = lambda kernel: [(float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3
+                                for r in sorted((r for r in csv.DictReader(open(trace_csv)) if kernel in r["Kernel_Name"]),
+                                                key=lambda r: int(r["Dispatch_Id"]))]
+    dur = durations(LIST_KERNEL)
     f_scale = REF_KIB / _reference(_counter_medians(fetch_csv, "FETCH_SIZE"))
     w_scale = REF_KIB / _reference(_counter_medians(write_csv, "WRITE_SIZE"))
     fetch = _list_rows(fetch_csv, "Counter_Value", "FETCH_SIZE")
@@ -261,8 +266,8 @@ def list_summary(trace_csv: str, fetch_csv: str, write_csv: str, sq_csv: str, ou
     sq = {n: _list_rows(sq_csv, "Counter_Value", n) for n in sq_names}
     nl_all = sum(len(l) for _, l in orders)
     med = statistics.median
-    lines = [f"# sgemv_list_kernel on the 224-GEMV decoder sequence, {LIST_PER_LAUNCH} GEMVs a launch "
-             f"(kernel sources {kernel_source_hash()})"]
+    lines = [f"# sgemv_list_kernel on the 224-GEMV decoder sequence, {LIST_PER_LAUNCH} GEMVs a launch, and "
+             f"sgemv_list_table_kernel, all 224 in one launch (kernel sources {kernel_source_hash()})"]
     lines += [f"# command: {c}" for c in commands]
     lines += [f"# HBM bytes = FETCH_SIZE x {f_scale:.4f} + WRITE_SIZE x {w_scale:.4f} (KiB, scaled by the 64 MiB "
               "reference copy of the same command); frac = algorithmic bytes / traced duration / 8 TB/s"]
@@ -292,6 +297,22 @@ def list_summary(trace_csv: str, fetch_csv: str, write_csv: str, sq_csv: str, ou
         for i in range(nl):
             lines.append(f"{i:6d} " + " ".join(f"{med(pos(sq[n], i)):16.0f}" for n in sq_names))
         first += nl
+    tdur = durations(TABLE_KERNEL)
+    if tdur:
+        nb = sum(b for _, b in orders[0][1])
+        g = sum(n for n, _ in orders[0][1])
+        tf = _list_rows(fetch_csv, "Counter_Value", "FETCH_SIZE", TABLE_KERNEL)
+        tw = _list_rows(write_csv, "Counter_Value", "WRITE_SIZE", TABLE_KERNEL)
+        hbm = (med(tf) * f_scale + med(tw) * w_scale) * 1024
+        lines += ["", "one table launch of all the GEMVs (sgemv_run_list_table)",
+                  f"{'launch':>6s} {'gemvs':>5s} {'alg_bytes':>11s} {'calls':>5s} {'avg_us':>8s} {'med_us':>8s} "
+                  f"{'frac_med':>8s} {'hbm_bytes':>11s} {'hbm/alg':>7s}",
+                  f"{0:6d} {g:5d} {nb:11d} {len(tdur):5d} {statistics.mean(tdur):8.2f} {med(tdur):8.2f} "
+                  f"{nb / (med(tdur) * 1e-6) / 8e12:8.4f} {int(hbm):11d} {hbm / nb:7.4f}",
+                  "SQ counters per dispatch (median):",
+                  f"{'launch':>6s} " + " ".join(f"{n:>16s}" for n in sq_names),
+                  f"{0:6d} " + " ".join(f"{med(_list_rows(sq_csv, 'Counter_Value', n, TABLE_KERNEL)):16.0f}"
+                                        for n in sq_names)]
     with open(out_txt, "w") as f:
         f.write("\n".join(lines) + "\n")
 

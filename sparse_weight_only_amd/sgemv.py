@@ -65,6 +65,16 @@ class Task(ctypes.Structure):
                 ("x_dev", ctypes.c_void_p), ("y_dev", ctypes.c_void_p)]
 
 
+class ListLaunch(ctypes.Structure):
+    """The launch of a task table (mirrors sgemv_list_launch)."""
+    _fields_ = [("table_bytes", ctypes.c_int64), ("lds_bytes", ctypes.c_int64), ("workgroups", ctypes.c_int64),
+                ("rows", ctypes.c_int32), ("row_width", ctypes.c_int32), ("tasks", ctypes.c_int32),
+                ("block", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
 MAX_GROUP = 32
 
 
@@ -83,6 +93,7 @@ def lib():
         P = ctypes.c_void_p
         i32, i64, u32, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_double
         D, PL, TK = ctypes.POINTER(Desc), ctypes.POINTER(Plan), ctypes.POINTER(Task)
+        LL = ctypes.POINTER(ListLaunch)
         sigs = {
             "sgemv_describe": [i32, i32, i32, P, D],
             "sgemv_select_groups": [P, i32, i32, i32, P, i32, f64, i32, i32, P],
@@ -99,6 +110,8 @@ def lib():
             "sgemv_plan_group": [TK, i32, i32, PL],
             "sgemv_run_list": [TK, i32, i32, P],
             "sgemv_plan_list": [TK, i32, i32, PL],
+            "sgemv_list_table": [TK, i32, i32, P, i64, LL],
+            "sgemv_run_list_table": [P, LL, P],
             "sgemv_probe_read": [P, i64, P, i64, u32, P],
             "sgemv_probe_empty": [i32, i32, P],
         }
@@ -309,6 +322,28 @@ def plan_list(tasks, B: int = 1) -> Plan:
     pl = Plan()
     _check(lib().sgemv_plan_list(_tasks(tasks), len(tasks), B, ctypes.byref(pl)), "sgemv_plan_list")
     return pl
+
+
+LIST_TABLE_MAX = 4096
+
+
+def list_table(tasks, B: int = 1):
+    """Plan one launch over up to LIST_TABLE_MAX one-vector GEMVs: returns
+    (table, launch), the table as a host uint8 array to be copied to device
+    memory, and the ListLaunch that sgemv_run_list_table takes with it."""
+    arr = _tasks(tasks)
+    launch = ListLaunch()
+    _check(lib().sgemv_list_table(arr, len(tasks), B, None, 0, ctypes.byref(launch)), "sgemv_list_table")
+    table = np.zeros(launch.table_bytes, dtype=np.uint8)
+    _check(lib().sgemv_list_table(arr, len(tasks), B, _ptr(table), table.size, ctypes.byref(launch)),
+           "sgemv_list_table")
+    return table, launch
+
+
+def run_list_table(table_dev: int, launch: ListLaunch, stream: int = 0) -> None:
+    """Enqueue the launch of a task table held at ``table_dev`` (device pointer as int)."""
+    _check(lib().sgemv_run_list_table(ctypes.c_void_p(table_dev), ctypes.byref(launch), ctypes.c_void_p(stream)),
+           "sgemv_run_list_table")
 
 
 def algorithmic_bytes(desc: Desc, B: int) -> int:

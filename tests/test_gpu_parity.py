@@ -602,8 +602,9 @@ def test_measurement_probes():
         sg.probe_empty(1, 100, s)
 
 
-def _run_list_checked(layers, Xs, guard=64):
-    """One sgemv_run_list launch over one-vector layers (guarded outputs)."""
+def _run_list_checked(layers, Xs, guard=64, table=False):
+    """One sgemv_run_list launch over one-vector layers (guarded outputs); with
+    ``table``, one sgemv_run_list_table launch from a device task table."""
     sentinel = np.uint16(0x7E5A)
     bufs, tasks, xs = [], [], []
     for layer, X in zip(layers, Xs):
@@ -613,7 +614,14 @@ def _run_list_checked(layers, Xs, guard=64):
         xs.append(x)
         bufs.append(ybuf)
         tasks.append((layer.desc, layer.blob.data_ptr(), x.data_ptr(), ybuf[guard:].data_ptr()))
-    sg.run_list(tasks, 1, torch.cuda.current_stream().cuda_stream)
+    if table:
+        host, launch = sg.list_table(tasks, 1)
+        say(f"  table launch: {launch.tasks} tasks, {launch.rows} rows of {launch.row_width}, "
+            f"{launch.workgroups} workgroups")
+        tdev = torch.from_numpy(host).cuda()
+        sg.run_list_table(tdev.data_ptr(), launch, torch.cuda.current_stream().cuda_stream)
+    else:
+        sg.run_list(tasks, 1, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     out = []
     for layer, ybuf in zip(layers, bufs):
@@ -653,6 +661,60 @@ def test_list_launch_exact_arithmetic():
         assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
     ys3 = _run_list_checked([lay for lay, _ in layers][::-1], Xs[::-1])[::-1]
     for y, y3 in zip(ys, ys3):
+        assert np.array_equal(y.view(np.uint16), y3.view(np.uint16))
+
+
+def test_list_table_exact_arithmetic():
+    """The layers of the exact-arithmetic list case through a task table in
+    device memory: bit-exact against the oracle, and the same bits as the
+    kernel-argument launch of the same tasks."""
+    rng = np.random.default_rng(63)
+    specs = [(600, 4096, 2), (33, 4096, 1), (1000, 2048, 1), (77, 11008, 2), (16, 256, 2), (300, 4096, 1),
+             (4100, 1024, 2), (5, 768, 1), (2000, 11008, 1), (40, 32768, 2), (17, 32768, 1)]
+    layers, Xs = [], []
+    for N, K, nk in specs:
+        gs = rng.choice([32, 64, 128, 256], N).astype(np.int32)
+        W = np.zeros((N, K), np.float16)
+        for g in np.unique(gs):
+            W[gs == g] = grid_weights(int((gs == g).sum()), K, nk, int(g), rng)
+        layers.append(make_layer(W, nk, gs))
+        X = np.zeros((1, K), np.float16)
+        idx = rng.choice(K, size=min(64, K), replace=False)
+        X[0, idx] = rng.choice([-1.0, 1.0], len(idx))
+        Xs.append(X)
+    say(f"case list table exact, {len(specs)} layers")
+    ys = _run_list_checked([lay for lay, _ in layers], Xs, table=True)
+    for (layer, ref), X, y in zip(layers, Xs, ys):
+        assert_bit_exact(y, ref.y(X)[0], (layer.desc.N, layer.desc.K, layer.desc.nk))
+    ys2 = _run_list_checked([lay for lay, _ in layers], Xs)
+    for y, y2 in zip(ys, ys2):
+        assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+
+
+def test_list_table_decoder_step():
+    """All 224 GEMVs of the 32-layer decoder set as one table launch (the
+    launch bench.py times; each GEMV with its own x and y, the weights of one
+    (shape, N:M) pair shared): within the tolerance of the oracle for every
+    GEMV, the same bits as five kernel-argument launches of 48 and on a
+    second table launch."""
+    made, layers, Xs = {}, [], []
+    for L in synth.cfg4():
+        key = (L.K, L.N, L.nk)
+        if key not in made:
+            W = L.W()
+            made[key] = make_layer(W, L.nk, group_sizes(L, W))
+        layers.append(made[key])
+        Xs.append(L.X(1))
+    say(f"case list table: decoder step, {len(layers)} GEMVs, {len(made)} weight sets")
+    ys = _run_list_checked([lay for lay, _ in layers], Xs, table=True)
+    for (layer, ref), X, y in zip(layers, Xs, ys):
+        assert ogemv.normalized_error(y, *ref.y(X)) <= TOL, (layer.desc.N, layer.desc.K, layer.desc.nk)
+    ys2 = []
+    for i in range(0, len(layers), sg.LIST_MAX):
+        ys2 += _run_list_checked([lay for lay, _ in layers[i: i + sg.LIST_MAX]], Xs[i: i + sg.LIST_MAX])
+    ys3 = _run_list_checked([lay for lay, _ in layers], Xs, table=True)
+    for y, y2, y3 in zip(ys, ys2, ys3):
+        assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
         assert np.array_equal(y.view(np.uint16), y3.view(np.uint16))
 
 

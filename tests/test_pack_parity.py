@@ -2,6 +2,7 @@
 
 Runs on the CPU: the library is loaded but no GPU call is made.
 """
+import ctypes
 import re
 import os
 
@@ -571,4 +572,82 @@ def test_list_plan_and_host_errors():
                        ((0x1000, 0x1008, 0x1000), E.SGEMV_EALIGN)]:
         with pytest.raises(sg.SgemvError) as e:
             sg.run_list([(d_small,) + ptrs], 1, 0)
+        assert e.value.code == code
+
+
+ROW = np.dtype([("blob", "<u8"), ("x", "<u8"), ("y", "<u8"), ("blob_bytes", "<u4"), ("off_offs", "<u4"),
+                ("off_perm", "<u4"), ("off_sz", "<u4"), ("N", "<i4"), ("cls1", "<i4"), ("cls2", "<i4"),
+                ("cls3", "<i4"), ("c_nk", "<u4"), ("n_wg", "<i4"), ("q", "<i4"), ("r", "<i4"), ("j0", "<i4"),
+                ("pad", "<i4")])
+
+
+def test_list_table_covers_every_block_once():
+    """sgemv_list_table: the rows of the table cover every row block of every
+    task exactly once, a task's rows are consecutive, and up to 48 tasks get
+    the shares of sgemv_plan_list. Beyond 48 tasks the workgroups grow with
+    the count (a share like that in a list of 48)."""
+    assert ROW.itemsize == 80
+    rng = np.random.default_rng(14)
+    shapes = [(4096, 4096), (11008, 4096), (4096, 11008), (40, 1024), (3000, 2048)]
+    descs = [sg.describe(N, K, nk, rng.choice([32, 64, 128, 256], N).astype(np.int32))
+             for N, K in shapes for nk in (1, 2)]
+    for count in (1, 7, 48, 49, 224, 300):
+        tasks = [(descs[int(i)], 0x100000 * (k + 1), 0x1000 * (k + 1), 0x2000 * (k + 1))
+                 for k, i in enumerate(rng.integers(0, len(descs), count))]
+        table, L = sg.list_table(tasks, 1)
+        assert (L.tasks, L.block) == (count, 512) and table.size == L.table_bytes == 80 * L.rows
+        rows = table.view(ROW)
+        seen = {}
+        for k, row in enumerate(rows):
+            key = int(row["y"])
+            assert row["j0"] % L.row_width == 0 and row["j0"] < row["n_wg"]
+            if key in seen:
+                assert seen[key][-1] == k - 1, "a task's rows are consecutive"
+            seen.setdefault(key, []).append(k)
+        assert len(seen) == count
+        total = 0
+        for (d, blob, x, y) in tasks:
+            ks = seen[y]
+            r0 = rows[ks[0]]
+            assert (int(r0["blob"]), int(r0["x"]), r0["N"]) == (blob, x, d.N)
+            n, q, r = int(r0["n_wg"]), int(r0["q"]), int(r0["r"])
+            assert len(ks) == -(-n // L.row_width) and n * q + r == d.n_blocks and q + (r > 0) <= 256
+            total += n
+        assert total == L.workgroups
+        if count <= sg.LIST_MAX:
+            assert L.workgroups == sg.plan_list(tasks, 1).grid
+        else:
+            assert L.workgroups > sg.plan_list(tasks[:48], 1).grid
+
+
+def test_list_table_host_errors():
+    """sgemv_list_table / sgemv_run_list_table host checks (no HIP call before them)."""
+    E = sg.sgemv
+    d = sg.describe(40, 1024, 2, np.full(40, 64, np.int32))
+    for tasks, B, code in [([], 1, E.SGEMV_EINVAL), ([(d, 0x1000, 0x1000, 0x1000)], 2, E.SGEMV_EINVAL),
+                           ([(d, 0x1000, 0x1000, 0x1000)] * (sg.LIST_TABLE_MAX + 1), 1, E.SGEMV_EINVAL),
+                           ([(d, 0, 0x1000, 0x1000)], 1, E.SGEMV_EINVAL),
+                           ([(d, 0x1001, 0x1000, 0x1000)], 1, E.SGEMV_EALIGN),
+                           ([(sg.describe_fp16(64, 1024, 2), 0x1000, 0x1000, 0x1000)], 1, E.SGEMV_EINVAL)]:
+        with pytest.raises(sg.SgemvError) as e:
+            sg.list_table(tasks, B)
+        assert e.value.code == code
+    # a table buffer smaller than the table
+    launch = sg.ListLaunch()
+    arr = sg.sgemv._tasks([(d, 0x1000, 0x1000, 0x1000)])
+    buf = np.zeros(79, np.uint8)
+    assert sg.lib().sgemv_list_table(arr, 1, 1, sg.sgemv._ptr(buf), buf.size, ctypes.byref(launch)) == E.SGEMV_ESIZE
+    assert sg.lib().sgemv_list_table(arr, 1, 1, None, 0, None) == E.SGEMV_EINVAL
+    # launches that no table describes, and a misaligned table
+    _, good = sg.list_table([(d, 0x1000, 0x1000, 0x1000)], 1)
+    for field, value in [("rows", 0), ("rows", 65536), ("row_width", 0), ("row_width", 33), ("block", 256),
+                         ("lds_bytes", 160 * 1024 + 1), ("table_bytes", 81)]:
+        bad = sg.ListLaunch.from_buffer_copy(good)
+        setattr(bad, field, value)
+        with pytest.raises(sg.SgemvError) as e:
+            sg.run_list_table(0x1000, bad, 0)
+        assert e.value.code == E.SGEMV_EINVAL, field
+    for ptr, code in [(0, E.SGEMV_EINVAL), (0x1008, E.SGEMV_EALIGN)]:
+        with pytest.raises(sg.SgemvError) as e:
+            sg.run_list_table(ptr, good, 0)
         assert e.value.code == code
