@@ -46,8 +46,9 @@ Beside the step, the same line reports
 * ``decoder``: the 224 GEMVs of a 32-layer 7B-shaped decoder (q, k, v, o
   4096 -> 4096, gate and up 4096 -> 11008, down 11008 -> 4096; 2:4 in the
   first and last 4 layers, 1:4 elsewhere), launched back to back on one
-  stream, each with its own x and y; 20 replays of a graph of the whole
-  sequence, once with one launch per GEMV, once with the launches a decode
+  stream, each with its own x and y; 4 replays (after one warm replay) of a
+  graph of 5 back-to-back passes over the whole sequence, once with one
+  launch per GEMV, once with the launches a decode
   step can group (q, k and v together; o; gate and up together; down: 4
   launches per layer, sgemv_run_group), and twice as task lists of 48 GEMVs
   per launch (sgemv_run_list: 5 launches), once in the sequence order and
@@ -537,7 +538,9 @@ def main():
     # ---- 224-GEMV decoder sequence, one launch per GEMV
     decoder = None
     if not args.no_decoder:
-        reps_dec = 20
+        # 5 sequences back to back per graph (as the per-layer figures time
+        # back-to-back launches), replayed 4 times after one warm replay
+        seqs_dec, reps_dec = 5, 4
         packed = {}
         for l in (0, 4):                        # one packed matrix per (shape, N:M)
             for m, (name, K, N) in enumerate(synth.LLAMA7B_MATS):
@@ -608,14 +611,20 @@ def main():
         def body_table():
             sg.run_list_table(table_dev.data_ptr(), table_launch, torch.cuda.current_stream(dev).cuda_stream)
 
-        ms_seq = timed(body_decoder, 1, reps_dec, 2)
-        ms_grp = timed(body_grouped, 1, reps_dec, 2)
-        ms_lst = timed(body_lists(lists), 1, reps_dec, 2)
-        ms_lsh = timed(body_lists(lists_shape), 1, reps_dec, 2)
-        ms_tab = timed(body_table, 1, reps_dec, 2)
+        def times(body):
+            def many():
+                for _ in range(seqs_dec):
+                    body()
+            return timed(many, seqs_dec, reps_dec, 1)
+
+        ms_seq = times(body_decoder)
+        ms_grp = times(body_grouped)
+        ms_lst = times(body_lists(lists))
+        ms_lsh = times(body_lists(lists_shape))
+        ms_tab = times(body_table)
         rate = lambda ms: {"us_per_sequence": round(ms * 1e3, 2), "GBps": round(dec_bytes / (ms * 1e-3) / 1e9, 1),
                            "pct_hbm_peak": round(100 * dec_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
-        decoder = {"gemvs": len(seq), "bytes": dec_bytes, "replays": reps_dec,
+        decoder = {"gemvs": len(seq), "bytes": dec_bytes, "sequences_per_graph": seqs_dec, "replays": reps_dec,
                    "one_launch_per_gemv": dict(launches=len(seq), **rate(ms_seq)),
                    "grouped_qkv_o_gateup_down": dict(launches=len(grouped), **rate(ms_grp)),
                    "task_list": dict(launches=len(lists), gemvs_per_launch=LIST_PER_LAUNCH, order="sequence",

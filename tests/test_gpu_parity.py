@@ -718,6 +718,33 @@ def test_list_table_decoder_step():
         assert np.array_equal(y.view(np.uint16), y3.view(np.uint16))
 
 
+def test_list_table_many_small_tasks():
+    """600 small layers (1 to 200 rows, 256 to 2048 columns, 2:4 and 1:4
+    mixed) and the degenerate-groups layer as one table launch: many tasks
+    of one or two workgroups, rows of the table shared by none; within the
+    tolerance of the oracle, the same bits as kernel-argument launches of 48."""
+    rng = np.random.default_rng(64)
+    layers, Xs = [], []
+    for i in range(600):
+        N, K = int(rng.integers(1, 201)), 256 * int(rng.integers(1, 9))
+        W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+        layers.append(make_layer(W, int(rng.choice([1, 2])), rng.choice([32, 64, 128, 256], N).astype(np.int32)))
+        Xs.append(rng.standard_normal((1, K)).astype(np.float16))
+    Wd, gs = degenerate_layer(3000, 2048, rng)
+    layers.append(make_layer(Wd, 2, gs))
+    X = rng.standard_normal((1, 2048))
+    X[:, :256] *= 2.0 ** -8
+    Xs.append(X.astype(np.float16))
+    say(f"case list table: {len(layers)} small layers")
+    ys = _run_list_checked([lay for lay, _ in layers], Xs, table=True)
+    for (layer, ref), X, y in zip(layers, Xs, ys):
+        assert ogemv.normalized_error(y, *ref.y(X)) <= TOL, (layer.desc.N, layer.desc.K)
+    for i in range(0, len(layers), sg.LIST_MAX):
+        part = _run_list_checked([lay for lay, _ in layers[i: i + sg.LIST_MAX]], Xs[i: i + sg.LIST_MAX])
+        for y, y2 in zip(ys[i: i + sg.LIST_MAX], part):
+            assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+
+
 def test_list_launch_mlp_layers_and_single_tasks():
     """The four MLP layers (up/down at 1:4 and 2:4, adaptive groups) as one
     list launch, and each alone (every workgroup then walks many blocks):
