@@ -16,7 +16,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-NEEDS_LAUNCHER = ["plan", "exported", "layer_run", "balanced_split", "error_paths", "fp16_form"]
+NEEDS_LAUNCHER = ["plan", "list_table", "exported", "layer_run", "balanced_split", "error_paths", "fp16_form"]
 LARGEST = ["decoder_set_every", "dense_ablation_mlp", "adaptive_mlp_configs", "11008-4096-1"]
 
 
