@@ -161,11 +161,13 @@ int sgemv_layout_fp16(const sgemv_desc* d, const uint16_t* vals16, const uint8_t
  * padding only for the rows of a last, partial row block):
  *  - rows sorted by group size (ascending, stable); row block b = sorted rows
  *    16b..16b+15; a piece = one row's kept elements in 64 dense columns;
- *  - codes [blocks][chunks][64 lanes][2*nk*4 bytes] and offsets
- *    [blocks][chunks][64 lanes][nk*4 bytes]: lane r + 16q of record (b, c)
- *    holds the piece of sorted row 16b + r in columns 256c + 64q .. +63, with
- *    a fixed nibble order inside each code dword and, at 1:4, a fixed 2-bit
- *    order inside the offset dword;
+ *  - 2:4: codes [blocks][chunks][64 lanes][16 bytes] and offsets
+ *    [blocks][chunks][64 lanes][8 bytes]; 1:4: one section
+ *    [blocks][chunks][64 lanes][12 bytes], a lane's 2 code dwords then its
+ *    offset dword, and an empty offset section; lane r + 16q of record
+ *    (b, c) holds the piece of sorted row 16b + r in columns 256c + 64q ..
+ *    +63, with a fixed nibble order inside each code dword and, at 1:4, a
+ *    fixed 2-bit order inside the offset dword;
  *  - perm int32[16*blocks]: original row of each sorted row, -1 for padding;
  *  - scale|zero<<16 words in records (b, c), each listing the rows of block b
  *    in order with their 256/g words of chunk c.

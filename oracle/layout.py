@@ -26,6 +26,8 @@ Bits of a piece
   2m of a little-endian 64-bit word (bytes unchanged); at 1:4 one dword with
   element m at bit 16*((m//4) % 2) + (REAL if m//4 < 2 else DUMMY)[m % 4],
   REAL = [0,4,10,14], DUMMY = [2,6,8,12].
+* at 1:4 a lane's piece is 12 bytes in the code section: its 2 code dwords,
+  then its offset dword (one load reads both); the offset section is empty.
 
 Dense ablation (nk = 4, every element kept, no offsets): a piece holds the
 64 elements of its columns in 8 dwords; dword 2t + h (t = 0..3, h = 0, 1)
@@ -43,8 +45,9 @@ block b in order, each row with its 256/g words of chunk c (its groups
 c*256/g .. (c+1)*256/g - 1). Padding rows have no words.
 
 Blob sections (each starting on a 256-byte boundary, in this order): codes
-[T][C][64][8*nk]; offsets [T][C][64][4*nk]; perm int32[16*T] (-1 for
-padding rows); scale/zero words, followed by 8 zero bytes.
+[T][C][64][8*nk] (1:4: [T][C][64][12], codes and offsets); offsets
+[T][C][64][8] (2:4 only); perm int32[16*T] (-1 for padding rows);
+scale/zero words, followed by 8 zero bytes.
 """
 import numpy as np
 
@@ -70,8 +73,14 @@ def off14_bit(m: int) -> int:
     return 16 * (t % 2) + (REAL if t < 2 else DUMMY)[e]
 
 
+def piece_code_bytes(nk: int) -> int:
+    """Bytes of a piece in the code section (1:4: codes and the offset dword)."""
+    return 12 if nk == 1 else 8 * nk
+
+
 def piece_offs_bytes(nk: int) -> int:
-    return 0 if nk == 4 else 4 * nk
+    """Bytes of a piece in the offset section (2:4 only)."""
+    return 8 if nk == 2 else 0
 
 
 def dense_dword_element(d: int, k: int) -> int:
@@ -85,7 +94,7 @@ def section_offsets(N: int, K: int, nk: int, n_groups: int) -> dict:
     T, C = -(-N // 16), K // 256
     records = T * C * 64
     off = {"codes": 0}
-    off["offs"] = _align(records * 8 * nk)
+    off["offs"] = _align(records * piece_code_bytes(nk))
     off["perm"] = _align(off["offs"] + records * piece_offs_bytes(nk))
     off["sz"] = _align(off["perm"] + 4 * 16 * T)
     off["blob_bytes"] = _align(off["sz"] + 4 * n_groups + 8)
@@ -138,6 +147,10 @@ def build(canon: dict) -> dict:
         # 16-byte slices: slice h of every lane, then slice h + 1
         codes = codes.reshape(T, C, 64, 2, 4).transpose(0, 1, 3, 2, 4)   # [T, C, h, lane, 4 dwords]
     offs = owp.reshape(T, 16, C, 4, -1).transpose(0, 2, 3, 1, 4)
+    if nk == 1:
+        # a lane's 2 code dwords, then its offset dword
+        codes = np.concatenate([codes, offs], axis=-1)                    # [T, C, q, r, 3]
+        offs = offs[..., :0]
     # scale/zero records
     sz_words = []
     for b in range(T):
@@ -176,11 +189,15 @@ def decode(blob: np.ndarray, N: int, K: int, nk: int, group_size):
     off = section_offsets(N, K, nk, n_groups)
     u32 = lambda at, n: np.frombuffer(blob[at: at + 4 * n].tobytes(), dtype="<u4")
     perm = np.frombuffer(blob[off["perm"]: off["perm"] + 64 * T].tobytes(), dtype="<i4")
-    cw = u32(off["codes"], T * C * 64 * 2 * nk).reshape(T, C, 64, 2 * nk)
+    pcw = piece_code_bytes(nk) // 4
+    cw = u32(off["codes"], T * C * 64 * pcw).reshape(T, C, 64, pcw)
     if nk == 4:
         cw = cw.reshape(T, C, 2, 64, 4).transpose(0, 1, 3, 2, 4).reshape(T, C, 64, 8)
-    now = piece_offs_bytes(nk) // 4
-    ow = u32(off["offs"], T * C * 64 * now).reshape(T, C, 64, now)
+    if nk == 1:
+        cw, ow = cw[..., :2], cw[..., 2:]
+    else:
+        now = piece_offs_bytes(nk) // 4
+        ow = u32(off["offs"], T * C * 64 * now).reshape(T, C, 64, now)
     szw = u32(off["sz"], n_groups)
     kpr = K * nk // 4
     q = np.zeros((N, kpr), dtype=np.uint8)
@@ -229,7 +246,7 @@ def section_offsets16(N: int, K: int, nk: int) -> dict:
     records = T * C * 64
     off = {"values": 0}
     off["offs"] = _align(records * 32 * nk)
-    off["perm"] = _align(off["offs"] + records * 4 * nk)
+    off["perm"] = _align(off["offs"] + records * 4 * nk)   # offsets stay a section of their own here
     off["blob_bytes"] = _align(off["perm"] + 4 * 16 * T)
     return off
 

@@ -16,6 +16,9 @@
 //  - offsets of a piece: 2:4 = the canonical 2-bit fields (element m at bits
 //    2m of a little-endian 64-bit word); 1:4 = one dword, element m at bit
 //    16*((m/4)%2) + (m/4 < 2 ? [0,4,10,14] : [2,6,8,12])[m%4];
+//  - at 1:4 a lane's piece is 12 bytes of the code section, its 2 code
+//    dwords and then its offset dword (one 12-byte load reads both), and the
+//    offset section is empty;
 //  - dense ablation (nk = 4, no offsets): code dword 2t + h holds positions
 //    2h and 2h + 1 of the 4 groups of piece columns 16t .. 16t + 15, element
 //    k = 2g + p at nibble [0,4,1,5,2,6,3,7][k]; a record stores dwords 0-3 of
@@ -107,7 +110,7 @@ extern "C" int sgemv_describe_fp16(int32_t N, int32_t K, int32_t nk, sgemv_desc*
   const int64_t records = (int64_t)T * C * 64;
   d.off_codes = 0;
   d.off_offs = align_up(records * piece_value16_bytes(nk));
-  d.off_perm = align_up(d.off_offs + records * piece_offs_bytes(nk));
+  d.off_perm = align_up(d.off_offs + records * piece_offs16_bytes(nk));
   d.off_sz = align_up(d.off_perm + 4 * (int64_t)T * kBlockRows);   // no words: the blob ends here
   d.blob_bytes = d.off_sz;
   if (d.blob_bytes >= ((int64_t)1 << 31)) return SGEMV_ESIZE;
@@ -122,7 +125,7 @@ extern "C" int sgemv_layout_fp16(const sgemv_desc* d, const uint16_t* vals16, co
   if (rc) return rc;
   if (memcmp(&chk, d, sizeof chk) != 0) return SGEMV_ESIZE;
   const int32_t N = d->N, K = d->K, nk = d->nk, T = d->n_blocks, C = d->chunks, kpr = K * nk / 4;
-  const int kpp = 16 * nk, pvb = piece_value16_bytes(nk), pob = piece_offs_bytes(nk);
+  const int kpp = 16 * nk, pvb = piece_value16_bytes(nk), pob = piece_offs16_bytes(nk);
   uint8_t* blob = (uint8_t*)blob_v;
   memset(blob, 0, (size_t)d->blob_bytes);
   int32_t* pm = (int32_t*)(blob + d->off_perm);
@@ -231,7 +234,7 @@ extern "C" int sgemv_layout(const sgemv_desc* d, const uint8_t* vals, const uint
             continue;
           }
           // codes: dwords of 8 elements with the nibble order of the N:M choice
-          for (int dw = 0; dw < pcb / 4; ++dw) {
+          for (int dw = 0; dw < 2 * nk; ++dw) {
             uint32_t word = 0;
             for (int k = 0; k < 8; ++k) {
               const int64_t j = e0 + 8 * dw + k;
@@ -251,7 +254,7 @@ extern "C" int sgemv_layout(const sgemv_desc* d, const uint8_t* vals, const uint
               const int t = m / 4, e = m % 4;
               word |= o << (16 * (t % 2) + (t < 2 ? kOff14Real[e] : kOff14Dummy[e]));
             }
-            memcpy(ob + rec * pob, &word, 4);
+            memcpy(cb + rec * pcb + 8, &word, 4);      // after the piece's 2 code dwords
           }
         }
         // scale|zero words of chunk c of this row

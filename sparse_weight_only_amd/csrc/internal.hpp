@@ -69,8 +69,13 @@ inline int bucket(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
 // Bytes of one piece (one row, 64 dense columns) in the code and offset sections.
 // nk = 4 is the dense ablation: every element kept, no offsets stored.
 inline bool valid_nk(int nk) { return nk == 1 || nk == 2 || nk == 4; }
-inline int piece_code_bytes(int nk) { return 8 * nk; }    // 16 (1:4), 32 (2:4) or 64 (dense) nibbles
-inline int piece_offs_bytes(int nk) { return nk == 4 ? 0 : 4 * nk; }   // 2 bits per kept element
+// Bytes of one lane's piece in the code section: 16 (1:4, with its offset
+// dword after the 8 bytes of codes), 32 (2:4) or 64 (dense) nibbles; in the
+// offset section: 8 at 2:4, none otherwise (the FP16-valued form keeps
+// 4 * nk bytes of offsets in a section of its own).
+inline int piece_code_bytes(int nk) { return nk == 1 ? 12 : 8 * nk; }
+inline int piece_offs_bytes(int nk) { return nk == 2 ? 8 : 0; }
+inline int piece_offs16_bytes(int nk) { return 4 * nk; }
 inline int piece_value16_bytes(int nk) { return 32 * nk; }                // FP16-valued form
 
 // Launch geometry for (chunks per row, row blocks, batch): how the column

@@ -22,8 +22,9 @@
 // waves w < crem and cpw - 1 after (fewer at the end of the row). Per wave:
 //  1. loads, all issued up front and in this order: the wave's x slice
 //     (16-byte loads, cached), then codes, offsets and scale|zero words of
-//     every chunk (non-temporal: the weights are read once); lanes without
-//     work read out of range and get zeros without touching memory;
+//     every chunk (non-temporal: the weights are read once; at 1:4 a lane's
+//     codes and offsets are one 12-byte piece, read by one load); lanes
+//     without work read out of range and get zeros without touching memory;
 //  2. the x slice goes to this wave's own LDS region (no barrier with other
 //     waves: a wave waits only for its own loads);
 //  3. per 64-column step: codes -> FP16 (q - z) exactly (0x6400 exponent
@@ -100,6 +101,14 @@ __device__ __forceinline__ u32x2 bload2(__amdgpu_buffer_rsrc_t r, uint32_t off, 
 template <int CPOL>
 __device__ __forceinline__ uint32_t bload1(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, CPOL);
+}
+// A 1:4 piece: 12 bytes, its 2 code dwords and its offset dword.
+struct Piece14 { u32x2 cv; uint32_t ov; };
+template <int CPOL>
+__device__ __forceinline__ Piece14 bload_piece14(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+  const u32x3 v = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, off, soff, CPOL));
+  return Piece14{u32x2{v.x, v.y}, v.z};
 }
 
 // A VGPR holding c whose value the compiler cannot see, so that (a & m) | c
@@ -277,8 +286,9 @@ __device__ __forceinline__ void sgemv_block(const KParams& p, const int rb) {
       cv[i] = bload4<kStream>(rbuf, p.off_codes + rec * CB, off);
       ov[i] = bload2<kStream>(rbuf, p.off_offs + rec * OB, off);
     } else {
-      cv[i] = bload2<kStream>(rbuf, p.off_codes + rec * CB, off);
-      ov[i] = bload1<kStream>(rbuf, p.off_offs + rec * OB, off);
+      const Piece14 pc = bload_piece14<kStream>(rbuf, p.off_codes + rec * 12u, off);
+      cv[i] = pc.cv;
+      ov[i] = pc.ov;
     }
     if constexpr (!V16) sv[i] = bload2<kStream>(rbuf, so, off);
     else sv[i] = u32x2{0u, 0u};
@@ -535,8 +545,9 @@ __device__ __forceinline__ void sgemv_block_rb(const KParams& p, const int rb0) 
         cv[j][i] = bload4<kStream>(rbuf, p.off_codes + rec * CB, off);
         ov[j][i] = bload2<kStream>(rbuf, p.off_offs + rec * OB, off);
       } else {
-        cv[j][i] = bload2<kStream>(rbuf, p.off_codes + rec * CB, off);
-        ov[j][i] = bload1<kStream>(rbuf, p.off_offs + rec * OB, off);
+        const Piece14 pc = bload_piece14<kStream>(rbuf, p.off_codes + rec * 12u, off);
+        cv[j][i] = pc.cv;
+        ov[j][i] = pc.ov;
       }
       sv[j][i] = bload2<kStream>(rbuf, so, off);
     }

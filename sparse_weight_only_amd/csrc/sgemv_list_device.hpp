@@ -106,8 +106,9 @@ __device__ __forceinline__ void issue_chunk(ChunkRegs<NK>& R, const KParams& p, 
     R.cv = bload4<kStream>(rbuf, lane_codes, g * 64u * CB + out);
     R.ov = bload2<kStream>(rbuf, lane_offs, p.off_offs + g * 64u * OB + out);
   } else {
-    R.cv = bload2<kStream>(rbuf, lane_codes, g * 64u * CB + out);
-    R.ov = bload1<kStream>(rbuf, lane_offs, p.off_offs + g * 64u * OB + out);
+    const Piece14 pc = bload_piece14<kStream>(rbuf, lane_codes, g * 64u * 12u + out);
+    R.cv = pc.cv;
+    R.ov = pc.ov;
   }
   R.sv = bload2<kStream>(rbuf, ic.sz_lane, ic.sz_base + (uint32_t)ic.chunk * ic.sz_step + out);
 }
@@ -200,7 +201,8 @@ __device__ __forceinline__ void list_stream(const KParams& p, int B0, int nbw) {
   const int nb = qq + (w < rr ? 1 : 0);
   const int total = nb * C;
 
-  const uint32_t lane_codes = (uint32_t)lane * (8u * NK), lane_offs = (uint32_t)lane * (4u * NK);
+  // a lane's piece: 16 bytes of codes (2:4) or 12 of codes and offsets (1:4)
+  const uint32_t lane_codes = (uint32_t)lane * (NK == 2 ? 16u : 12u), lane_offs = (uint32_t)lane * (4u * NK);
   IssueCursor ic;
   ic.blk = b0;
   ic.chunk = 0;

@@ -75,17 +75,21 @@ def test_hand_placed_bytes_1of4():
              "gptr": np.array([0, 1], np.int32)}
     L = layout.build(canon)
     off = L["offsets"]
-    assert (off["codes"], off["offs"], off["perm"], off["sz"], off["blob_bytes"]) == (0, 512, 768, 1024, 1280)
+    # 64 lanes x 12 bytes (2 code dwords, then the offset dword) = 768 bytes of
+    # codes; the offset section is empty; 64 bytes of perm; the scale|zero word
+    assert (off["codes"], off["offs"], off["perm"], off["sz"], off["blob_bytes"]) == (0, 768, 768, 1024, 1280)
     blob = L["blob"]
     # lane 16 = columns 64..127 = elements 16..31; dword 0 = elements 16..23 with
     # codes 0..7, element k at nibble [0,1,4,5,2,3,6,7][k]: nibbles 0..7 hold
     # 0,1,4,5,2,3,6,7 -> 0x76325410
-    assert u32_at(blob, 16 * 8) == 0x76325410
-    # lane 0 offsets: element m = 4t + e has offset t and sits at bit
-    # 16*(t%2) + ([0,4,10,14] if t < 2 else [2,6,8,12])[e]:
+    assert u32_at(blob, 16 * 12) == 0x76325410
+    # lane 0 offsets, its third dword: element m = 4t + e has offset t and sits
+    # at bit 16*(t%2) + ([0,4,10,14] if t < 2 else [2,6,8,12])[e]:
     # t=1 -> 1 at bits 16,20,26,30 = 0x44110000; t=2 -> 2 at bits 2,6,8,12 =
     # 0x00002288; t=3 -> 3 at bits 18,22,24,28 = 0x33CC0000
-    assert u32_at(blob, 512) == 0x77DD2288
+    assert u32_at(blob, 8) == 0x77DD2288
+    # lane 1 (the padding row 1, no data) is all zero, then lane 16's codes
+    assert blob[12: 24].tolist() == [0] * 12
     assert u32_at(blob, 1024) == 0x48003C00
     assert np.frombuffer(blob[768: 832].tobytes(), "<i4").tolist() == [0] + [-1] * 15
 
