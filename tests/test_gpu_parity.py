@@ -745,6 +745,27 @@ def test_list_table_many_small_tasks():
             assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
 
 
+def test_list_table_most_tasks():
+    """SGEMV_LIST_TABLE_MAX (4096) layers of 1 to 48 rows and 256 or 512
+    columns, 2:4 and 1:4 mixed, as one table launch: within the tolerance of
+    the oracle, and the same bits for the first 48 as a kernel-argument
+    launch of them."""
+    rng = np.random.default_rng(65)
+    layers, Xs = [], []
+    for i in range(sg.LIST_TABLE_MAX):
+        N, K = int(rng.integers(1, 49)), 256 * int(rng.integers(1, 3))
+        W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+        layers.append(make_layer(W, int(rng.choice([1, 2])), rng.choice([32, 64, 128, 256], N).astype(np.int32)))
+        Xs.append(rng.standard_normal((1, K)).astype(np.float16))
+    say(f"case list table: {len(layers)} layers, the most a table takes")
+    ys = _run_list_checked([lay for lay, _ in layers], Xs, table=True)
+    for (layer, ref), X, y in zip(layers, Xs, ys):
+        assert ogemv.normalized_error(y, *ref.y(X)) <= TOL, (layer.desc.N, layer.desc.K)
+    part = _run_list_checked([lay for lay, _ in layers[:sg.LIST_MAX]], Xs[:sg.LIST_MAX])
+    for y, y2 in zip(ys, part):
+        assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+
+
 def test_list_launch_mlp_layers_and_single_tasks():
     """The four MLP layers (up/down at 1:4 and 2:4, adaptive groups) as one
     list launch, and each alone (every workgroup then walks many blocks):
